@@ -70,6 +70,13 @@ def _scores(q_rows, k_all, s, rows, causal):
     return S
 
 
+def _visible(rows, N, causal):
+    """Number of leading keys any of these query rows can see.  Under the causal
+    mask keys after the last row have probability exactly 0 for every row of the
+    block, so leaving them out changes no value."""
+    return int(np.max(rows)) + 1 if causal else N
+
+
 def _softmax_rows(S):
     """Row softmax with max subtraction; returns P and the row log-sum-exp."""
     m = S.max(axis=1, keepdims=True)
@@ -128,8 +135,9 @@ def attention_fwd_ref(q, k, v, scale, causal, rows=None):
             r_all = pick(b, h)
             for a in range(0, R, _ROW_BLOCK):
                 r = r_all[a:a + _ROW_BLOCK]
-                P, lse = _softmax_rows(_scores(q[b, h, r], k[b, kv], s, r, causal))
-                O[b, h, a:a + len(r)] = P @ v[b, kv]
+                n = _visible(r, N, causal)
+                P, lse = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
+                O[b, h, a:a + len(r)] = P @ v[b, kv, :n]
                 LSE[b, h, a:a + len(r)] = lse
     return O, LSE
 
@@ -164,22 +172,25 @@ def attention_bwd_ref(q, k, v, do, scale, causal, rows=None, key_rows=None):
                 r_all = qpick(b, h)
                 for a in range(0, R, _ROW_BLOCK):
                     r = r_all[a:a + _ROW_BLOCK]
-                    P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv], s, r, causal))
-                    dP = do[b, h, r] @ v[b, kv].T
+                    n = _visible(r, N, causal)
+                    P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
+                    dP = do[b, h, r] @ v[b, kv, :n].T
                     dS = _softmax_vjp(P, dP, N)
-                    dQ[b, h, a:a + len(r)] = s * (dS @ k[b, kv])
+                    dQ[b, h, a:a + len(r)] = s * (dS @ k[b, kv, :n])
             # dK/dV on the selected key rows (and dQ on all rows when full).
             kr = kpick(b, kv)
             start = int(kr.min()) if (causal and not full_q) else 0
             for a in range(start, N, _ROW_BLOCK):
                 r = np.arange(a, min(a + _ROW_BLOCK, N))
-                P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv], s, r, causal))
-                dP = do[b, h, r] @ v[b, kv].T
+                n = _visible(r, N, causal)
+                P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
+                dP = do[b, h, r] @ v[b, kv, :n].T
                 dS = _softmax_vjp(P, dP, N)
                 if full_q:
-                    dQ[b, h, r] = s * (dS @ k[b, kv])
-                dV[b, kv] += P[:, kr].T @ do[b, h, r]
-                dK[b, kv] += s * (dS[:, kr].T @ q[b, h, r])
+                    dQ[b, h, r] = s * (dS @ k[b, kv, :n])
+                sel = np.nonzero(kr < n)[0]
+                dV[b, kv, sel] += P[:, kr[sel]].T @ do[b, h, r]
+                dK[b, kv, sel] += s * (dS[:, kr[sel]].T @ q[b, h, r])
     return dQ, dK, dV
 
 
