@@ -46,6 +46,9 @@ examples (``tests/golden``), exact identities and PyTorch float64 autograd.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 EXPLICIT_JACOBIAN_MAX_N = 256
@@ -116,6 +119,70 @@ def _row_sets(rows, B, H, N):
     return lambda b, h: rows[b, h]
 
 
+def _head_fwd(qh, kh, vh, s, causal, r_all):
+    """O and LSE of one head on the query rows r_all."""
+    N = kh.shape[0]
+    O = np.empty((len(r_all), qh.shape[1])); LSE = np.empty(len(r_all))
+    for a in range(0, len(r_all), _ROW_BLOCK):
+        r = r_all[a:a + _ROW_BLOCK]
+        n = _visible(r, N, causal)
+        P, lse = _softmax_rows(_scores(qh[r], kh[:n], s, r, causal))
+        O[a:a + len(r)] = P @ vh[:n]
+        LSE[a:a + len(r)] = lse
+    return O, LSE
+
+
+def _head_bwd(qh, kh, vh, doh, s, causal, r_sel, kr):
+    """One query head's share of the backward pass.
+
+    Returns dQ on the rows r_sel (all rows when r_sel is None) and this head's
+    contribution to dK/dV on the key rows kr.
+    """
+    N, d = kh.shape
+    full_q = r_sel is None
+    dQ = np.empty((N if full_q else len(r_sel), d))
+    dK = np.zeros((len(kr), d)); dV = np.zeros((len(kr), d))
+    if not full_q:
+        for a in range(0, len(r_sel), _ROW_BLOCK):
+            r = r_sel[a:a + _ROW_BLOCK]
+            n = _visible(r, N, causal)
+            P, _ = _softmax_rows(_scores(qh[r], kh[:n], s, r, causal))
+            dP = doh[r] @ vh[:n].T
+            dS = _softmax_vjp(P, dP, N)
+            dQ[a:a + len(r)] = s * (dS @ kh[:n])
+    # dK/dV need every query row that sees a selected key: under the causal mask
+    # rows before the first selected key contribute exactly zero.
+    start = int(kr.min()) if (causal and not full_q) else 0
+    for a in range(start, N, _ROW_BLOCK):
+        r = np.arange(a, min(a + _ROW_BLOCK, N))
+        n = _visible(r, N, causal)
+        P, _ = _softmax_rows(_scores(qh[r], kh[:n], s, r, causal))
+        dP = doh[r] @ vh[:n].T
+        dS = _softmax_vjp(P, dP, N)
+        if full_q:
+            dQ[r] = s * (dS @ kh[:n])
+        sel = np.nonzero(kr < n)[0]
+        dV[sel] += P[:, kr[sel]].T @ doh[r]
+        dK[sel] += s * (dS[:, kr[sel]].T @ qh[r])
+    return dQ, dK, dV
+
+
+def _map_heads(fn, jobs, n_keys):
+    """Runs independent per-head jobs, concurrently when there are several
+    large ones.
+
+    Heads share nothing, so running them on several threads changes no value;
+    BLAS is limited to one thread per job while the pool is active.
+    """
+    workers = min(len(jobs), len(os.sched_getaffinity(0))) if n_keys >= 1024 else 1
+    if workers <= 1:
+        return [fn(*j) for j in jobs]
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(lambda j: fn(*j), jobs))
+
+
 def attention_fwd_ref(q, k, v, scale, causal, rows=None):
     """Forward oracle.  Returns (O, LSE) in float64.
 
@@ -128,17 +195,12 @@ def attention_fwd_ref(q, k, v, scale, causal, rows=None):
     s = float(scale)
     pick = _row_sets(rows, B, H, N)
     R = len(pick(0, 0))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    res = _map_heads(_head_fwd, [(q[b, h], k[b, h // g], v[b, h // g], s, causal, pick(b, h)) for b, h in heads], N)
     O = np.empty((B, H, R, d)); LSE = np.empty((B, H, R))
-    for b in range(B):
-        for h in range(H):
-            kv = h // g
-            r_all = pick(b, h)
-            for a in range(0, R, _ROW_BLOCK):
-                r = r_all[a:a + _ROW_BLOCK]
-                n = _visible(r, N, causal)
-                P, lse = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
-                O[b, h, a:a + len(r)] = P @ v[b, kv, :n]
-                LSE[b, h, a:a + len(r)] = lse
+    for (b, h), (o, lse) in zip(heads, res):
+        O[b, h] = o
+        LSE[b, h] = lse
     return O, LSE
 
 
@@ -147,9 +209,8 @@ def attention_bwd_ref(q, k, v, do, scale, causal, rows=None, key_rows=None):
 
     ``rows`` selects the query rows of dQ (as in ``attention_fwd_ref``);
     ``key_rows`` selects the key rows of dK/dV (None, [Rk] or [B, Hkv, Rk]).
-    dK/dV of a key need every query row that sees it, so those rows are all
-    visited; under the causal mask rows i < min(selected keys) contribute
-    exactly zero and are skipped.
+    GQA: dK/dV of a KV head sum the contributions of its query heads, added in
+    ascending head order.
     """
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64); do = np.asarray(do, np.float64)
@@ -161,36 +222,16 @@ def attention_bwd_ref(q, k, v, do, scale, causal, rows=None, key_rows=None):
     qpick = _row_sets(rows, B, H, N)
     kpick = _row_sets(key_rows, B, Hkv, N)
     R = len(qpick(0, 0)); Rk = len(kpick(0, 0))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    jobs = [(q[b, h], k[b, h // g], v[b, h // g], do[b, h], s, causal,
+             None if rows is None else qpick(b, h), kpick(b, h // g)) for b, h in heads]
+    res = _map_heads(_head_bwd, jobs, N)
     dQ = np.empty((B, H, R, d))
     dK = np.zeros((B, Hkv, Rk, d)); dV = np.zeros((B, Hkv, Rk, d))
-    full_q = rows is None
-    for b in range(B):
-        for h in range(H):
-            kv = h // g
-            # dQ on the selected query rows.
-            if not full_q:
-                r_all = qpick(b, h)
-                for a in range(0, R, _ROW_BLOCK):
-                    r = r_all[a:a + _ROW_BLOCK]
-                    n = _visible(r, N, causal)
-                    P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
-                    dP = do[b, h, r] @ v[b, kv, :n].T
-                    dS = _softmax_vjp(P, dP, N)
-                    dQ[b, h, a:a + len(r)] = s * (dS @ k[b, kv, :n])
-            # dK/dV on the selected key rows (and dQ on all rows when full).
-            kr = kpick(b, kv)
-            start = int(kr.min()) if (causal and not full_q) else 0
-            for a in range(start, N, _ROW_BLOCK):
-                r = np.arange(a, min(a + _ROW_BLOCK, N))
-                n = _visible(r, N, causal)
-                P, _ = _softmax_rows(_scores(q[b, h, r], k[b, kv, :n], s, r, causal))
-                dP = do[b, h, r] @ v[b, kv, :n].T
-                dS = _softmax_vjp(P, dP, N)
-                if full_q:
-                    dQ[b, h, r] = s * (dS @ k[b, kv, :n])
-                sel = np.nonzero(kr < n)[0]
-                dV[b, kv, sel] += P[:, kr[sel]].T @ do[b, h, r]
-                dK[b, kv, sel] += s * (dS[:, kr[sel]].T @ q[b, h, r])
+    for (b, h), (dq, dk, dv) in zip(heads, res):
+        dQ[b, h] = dq
+        dK[b, h // g] += dk
+        dV[b, h // g] += dv
     return dQ, dK, dV
 
 
