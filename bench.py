@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of exact attention forward + backward on one MI355X (gfx950).
+
+One step is one pass of the whole path on one batch of synthetic input that is
+already resident in HBM: ``fa_fwd`` followed by the three backward phases
+(``fa_bwd_preprocess``, ``fa_bwd_main``, ``fa_bwd_finalize``, i.e. ``fa_bwd``),
+all on one stream.  W untimed warm-up steps, then exactly K timed steps
+bracketed by ``torch.cuda.synchronize()``.  Prints ONE JSON line on stdout.
+
+Throughput uses the algorithmic flop count (what the method must compute; the
+masked half under the causal mask is work it avoids):
+    F_fwd = 4 B H N^2 d (x 1/2 if causal),  F_bwd = 2.5 F_fwd,  F_tot = 3.5 F_fwd.
+
+HIP events recorded between the kernels on the launch stream give each
+kernel's average duration; the dominant kernel's achieved rate is reported
+against the MI355X dense bf16 MFMA peak (2.5 PFLOP/s published).  The CPU
+oracle is timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_bwd_main_llama2_7b_causal_n4096_d128.json")
+KERNEL_SOURCES = ["tiled_attention_14_amd/csrc/fa_bwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops(w):
+    f_fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return f_fwd, 2.5 * f_fwd, 3.5 * f_fwd
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch of the backward main kernel from the committed
+    counter summary, or None when it is missing or the kernel source changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=12.0):
+    """Times the float64 oracle (unchanged) on whole (batch, head) slices of the
+    workload, as many rounds of `cores` heads as fit in about `budget_s`."""
+    import numpy as np
+    from oracle import attention_bwd_ref, attention_fwd_ref
+    cores = len(os.sched_getaffinity(0))
+    g = w.H // w.Hkv
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_total, f_total = 0, 0.0, 0.0
+    q, k, v, do = inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do")
+    while done < len(heads):
+        batch = heads[done:done + cores]
+        qs = np.stack([q[b, h] for b, h in batch])[None]
+        ks = np.stack([k[b, h // g] for b, h in batch])[None]
+        vs = np.stack([v[b, h // g] for b, h in batch])[None]
+        ds = np.stack([do[b, h] for b, h in batch])[None]
+        t0 = time.perf_counter()
+        attention_fwd_ref(qs, ks, vs, w.scale, w.causal)
+        attention_bwd_ref(qs, ks, vs, ds, w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        f_total += 3.5 * 4.0 * len(batch) * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+        done += len(batch)
+        if t_total >= budget_s:
+            break
+    return {"value": f_total / t_total / 1e12, "unit": "TFLOP/s", "cores": min(cores, done),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) slices, full fwd+bwd in float64 "
+                      f"({t_total:.1f} s on the host CPU)"}
+
+
+def main():
+    from tiled_attention_14_amd import synth
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the attention path here is single-GPU "
+              f"(--gpus {args.gpus}, WORLD_SIZE={world} requested); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from tiled_attention_14_amd import fa
+
+    w = synth.WORKLOADS[args.workload]
+    dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
+    def up(name):
+        if inp.bits is not None:
+            return torch.from_numpy(inp.bits[name].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(inp.vals[name]).to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_buf, ws, ws_n = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, dt, dev)
+    stream = torch.cuda.current_stream()
+    sargs = (w.B, w.H, w.Hkv, w.N, w.d)
+
+    def step(ev=None):
+        if ev is not None: ev[0].record(stream)
+        st = fa.fa_fwd(q, k, v, o, lse, *sargs, w.scale, w.causal, dt, stream)
+        if ev is not None: ev[1].record(stream)
+        st |= fa.fa_bwd_preprocess(o, do, dq, *sargs, dt, ws, ws_n, stream)
+        if ev is not None: ev[2].record(stream)
+        st |= fa.fa_bwd_main(q, k, v, do, lse, dq, dk, dv, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
+        if ev is not None: ev[3].record(stream)
+        st |= fa.fa_bwd_finalize(dq, *sargs, dt, ws, ws_n, stream)
+        if ev is not None: ev[4].record(stream)
+        if st != fa.FA_OK:
+            raise RuntimeError("attention call failed")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warm-up steps done")
+
+    # Timed region: exactly K steps, no events (wall clock between synchronizations).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps: {wall * 1e3 / args.steps:.3f} ms/step")
+
+    # Per-kernel durations: the same K steps again with events between the kernels.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    names = ["fa_fwd_kernel", "fa_bwd_pre_kernel", "fa_bwd_main_kernel", "fa_bwd_dq_cvt_kernel"]
+    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    log("[bench] kernel averages (ms): " + ", ".join(f"{n}={t:.4f}" for n, t in per.items()))
+
+    f_fwd, f_bwd, f_tot = flops(w)
+    ms = wall * 1e3 / args.steps
+    value = f_tot / (ms * 1e-3) / 1e12
+    t_fwd = per["fa_fwd_kernel"]
+    t_bwd = per["fa_bwd_pre_kernel"] + per["fa_bwd_main_kernel"] + per["fa_bwd_dq_cvt_kernel"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # Dominant kernel: the backward main kernel carries all five products of the
+    # backward pass (S recompute, dP, dV, dK, dQ), i.e. F_bwd.
+    dom = max(("fa_fwd_kernel", "fa_bwd_main_kernel"), key=lambda n: per[n])
+    dom_flops = f_fwd if dom == "fa_fwd_kernel" else f_bwd
+    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    traffic = traffic_for_current_kernel() if (dom == "fa_bwd_main_kernel" and w.name == synth.HEADLINE) else None
+
+    # The preprocess is bound by HBM: it reads O and dO and writes D and the zeroed dQ accumulator.
+    el = 2 if w.dtype == "bf16" else 4
+    pre_bytes = 2 * w.B * w.H * w.N * w.d * el + 4 * w.B * w.H * w.N + (4 * w.B * w.H * w.N * w.d)
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q, K, V, dO; bf16-rounded)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "fwd_ms": round(t_fwd, 4),
+        "bwd_ms": round(t_bwd, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in per.items()},
+        "bwd_preprocess_gbs": round(pre_bytes / (per["fa_bwd_pre_kernel"] * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * fa.h — C ABI of the exact softmax attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact softmax attention
+ *
+ *     O = softmax(scale * Q K^T) V
+ *
+ * (the materialised attention of the "standard attention" code block in
+ * "FlashAttention V2深度解析：反向传播显存优化让大模型训练不再OOM", section
+ * "Attention反向传播的「内存泄漏」难题"), without ever storing the N x N score
+ * matrix: the forward pass tiles Q and K/V and keeps a running row maximum and
+ * exponential sum (the online / incremental softmax of "【词汇专栏】FlashAttention",
+ * section 2.2 在线Softmax, and of "FlashAttention 在昇腾NPU上到底快在哪",
+ * section 三、增量 Softmax), and saves one log-sum-exp per query row.  The
+ * backward pass recomputes the probabilities from Q, K and that log-sum-exp
+ * instead of reading a stored attention matrix (the recomputation principle of
+ * "FlashAttention V2深度解析", section 改进1：IO感知的算子调度), so its extra memory
+ * is O(N).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (memory of the current HIP device),
+ *    16-byte aligned, densely packed, row-major:
+ *        q, o, dO, dq : [B, H,   N, d]
+ *        k, v, dk, dv : [B, Hkv, N, d]
+ *        lse          : [B, H,   N]      float32
+ *    Element type of q, k, v, o, dO, dq, dk, dv is given by `dtype`.
+ *  - GQA / MQA: query head h reads KV head h / (H / Hkv) (contiguous groups);
+ *    H must be a multiple of Hkv.  Hkv == H is ordinary multi-head attention.
+ *  - `causal` != 0 applies the square causal mask: key j is visible to query i
+ *    iff j <= i.
+ *  - d must be 64 or 128.  N may be any value >= 1 (ragged tails are masked).
+ *  - `scale` multiplies Q K^T (typically 1/sqrt(d)); it must be finite and > 0.
+ *  - lse[b,h,i] is the natural-log log-sum-exp of the scaled, masked scores of
+ *    query row i.
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    backward workspace.  The library never allocates device memory, keeps no
+ *    state across calls, and is safe to call from several threads.  Outputs must
+ *    not alias inputs.
+ *  - All work is enqueued on `stream` (0 = the default stream) and is
+ *    asynchronous: a call returns once its kernels are launched.  Faults inside
+ *    kernels surface at the caller's next synchronisation.
+ *  - Errors: arguments are validated before anything is launched; an invalid
+ *    call returns a non-zero status and enqueues nothing.  Nothing is printed,
+ *    thrown or aborted across this boundary.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_BF16 = 0, /* bfloat16 storage, float32 accumulation and statistics */
+  FA_F32 = 1   /* float32 storage and arithmetic throughout             */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad sizes, H % Hkv != 0, scale not finite and > 0 */
+  FA_ERR_UNSUPPORTED = 2, /* d not in {64, 128}, unknown dtype                                   */
+  FA_ERR_WORKSPACE = 3,   /* workspace null, misaligned or smaller than fa_bwd_workspace_size    */
+  FA_ERR_HIP = 4          /* a kernel launch failed                                              */
+} fa_status_t;
+
+/*
+ * Forward pass.  Writes o = softmax(scale * q k^T) v and lse.
+ * Inputs q, k, v; outputs o and lse (see layouts above).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v,
+                   void* o, float* lse,
+                   int B, int H, int Hkv, int N, int d,
+                   float scale, int causal, fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: one float32 per
+ * query row (D_i = sum_c dO_ic * O_ic) plus, for FA_BF16, a float32 dQ
+ * accumulator [B, H, N, d].  O(N) in the sequence length.  Returns 0 when the
+ * sizes are invalid.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype);
+
+/*
+ * Backward pass of L = sum(dO * O) for the forward above.  Inputs q, k, v, the
+ * forward's o and lse, and dO; outputs dq, dk, dv (same dtype and layout as
+ * q, k, v).  dk and dv sum over the query heads of each GQA group.  `workspace`
+ * is device memory of at least fa_bwd_workspace_size(...) bytes, 256-byte
+ * aligned, owned by the caller and not touched by anything else until the
+ * enqueued work has finished; its contents on entry do not matter.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v,
+                   const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv,
+                   int B, int H, int Hkv, int N, int d,
+                   float scale, int causal, fa_dtype_t dtype,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The three phases of fa_bwd, callable one by one (same arguments, layouts,
+ * workspace and error rules as fa_bwd); enqueued in this order on one stream
+ * they do exactly what fa_bwd does.  They exist so that callers and
+ * benchmarks can time or schedule the phases separately.
+ *
+ * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic into the workspace, and zeroes
+ *   the float32 dQ accumulator (the workspace for FA_BF16, dq itself for
+ *   FA_F32).  Reads o and dO.
+ * fa_bwd_main: recomputes P from q, k and lse and accumulates dV = P^T dO,
+ *   dK = scale dS^T q and scale dS k into the dQ accumulator, with
+ *   dS = P * (dO v^T - D).  Writes dk and dv; needs the preprocess first.
+ * fa_bwd_finalize: FA_BF16 converts the dQ accumulator into dq; FA_F32 does
+ *   nothing (dq already holds the result).
+ */
+fa_status_t fa_bwd_preprocess(const void* o, const void* dO, void* dq,
+                              int B, int H, int Hkv, int N, int d, fa_dtype_t dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+fa_status_t fa_bwd_main(const void* q, const void* k, const void* v,
+                        const void* dO, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        int B, int H, int Hkv, int N, int d,
+                        float scale, int causal, fa_dtype_t dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+fa_status_t fa_bwd_finalize(void* dq, int B, int H, int Hkv, int N, int d, fa_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,167 @@
+"""The C-ABI library loads, exports every symbol ``include/fa.h`` declares, and
+rejects invalid calls with the documented status before anything is launched.
+These calls never reach a kernel, so they run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_attention_14_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from tiled_attention_14_amd import build
+        build.build()
+    return fa.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert names == ["fa_bwd", "fa_bwd_finalize", "fa_bwd_main", "fa_bwd_preprocess", "fa_bwd_workspace_size",
+                     "fa_fwd", "fa_status_string"]
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        s = fa.fa_status_string(st)
+        assert s.startswith("FA_OK" if st == 0 else "FA_ERR")
+    assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
+
+
+GOOD = dict(B=1, H=4, Hkv=2, N=100, d=64, scale=0.125, causal=1, dtype=fa.FA_BF16)
+P = 0x10000  # a fake, 256-byte aligned address: these calls must never dereference it
+
+
+def _fwd(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 5)
+    return fa.fa_fwd(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], 0)
+
+
+def _bwd(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 9)
+    ws = a.pop("ws", P)
+    wsb = a.pop("wsb", 1 << 40)
+    return fa.fa_bwd(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                     ws, wsb, 0)
+
+
+def _pre(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 3)
+    return fa.fa_bwd_preprocess(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["dtype"],
+                                a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
+
+
+def _main(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 8)
+    return fa.fa_bwd_main(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                          a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
+
+
+def _fin(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P])
+    return fa.fa_bwd_finalize(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["dtype"],
+                              a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd, _main])
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20), fa.FA_ERR_INVALID_ARG),
+])
+def test_invalid_arguments(lib, call, kw, status):
+    assert call(**kw) == status
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_fwd_null_and_misaligned_pointers(lib, i):
+    ptrs = [P] * 5
+    ptrs[i] = None
+    assert _fwd(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+    ptrs[i] = P + 8
+    assert _fwd(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_bwd_null_and_misaligned_pointers(lib, i):
+    ptrs = [P] * 9
+    ptrs[i] = None
+    assert _bwd(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+    ptrs[i] = P + 4
+    assert _bwd(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("call", [_pre, _fin])
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG), (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), fa.FA_ERR_INVALID_ARG), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED), (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws=P + 64), fa.FA_ERR_WORKSPACE), (dict(wsb=16), fa.FA_ERR_WORKSPACE),
+])
+def test_phase_invalid_arguments(lib, call, kw, status):
+    assert call(**kw) == status
+
+
+@pytest.mark.parametrize("call,n", [(_pre, 3), (_main, 8), (_fin, 1)])
+def test_phase_null_and_misaligned_pointers(lib, call, n):
+    for i in range(n):
+        ptrs = [P] * n
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+        ptrs[i] = P + 2
+        assert call(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_errors(lib):
+    need = fa.fa_bwd_workspace_size(1, 4, 2, 100, 64, fa.FA_BF16)
+    assert _bwd(ws=None) == fa.FA_ERR_WORKSPACE
+    assert _bwd(ws=P + 16) == fa.FA_ERR_WORKSPACE          # not 256-byte aligned
+    assert _bwd(wsb=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_workspace_size_is_linear_in_n(lib):
+    for dt, per_row in ((fa.FA_BF16, lambda d: 4 * (1 + d)), (fa.FA_F32, lambda d: 4)):
+        for (B, H, Hkv, N, d) in [(1, 1, 1, 1, 64), (2, 32, 32, 4096, 128), (1, 64, 8, 8192, 128),
+                                  (1, 8, 8, 65536, 128), (3, 4, 2, 129, 64)]:
+            n = fa.fa_bwd_workspace_size(B, H, Hkv, N, d, dt)
+            rows = B * H * N
+            exact = per_row(d) * rows
+            assert exact <= n <= exact + 256, (dt, B, H, N, d, n)
+    # O(N): doubling N doubles the workspace (up to alignment padding), never quadruples it.
+    a = fa.fa_bwd_workspace_size(1, 8, 8, 32768, 128, fa.FA_BF16)
+    b = fa.fa_bwd_workspace_size(1, 8, 8, 65536, 128, fa.FA_BF16)
+    assert abs(b - 2 * a) <= 512
+    assert fa.fa_bwd_workspace_size(0, 1, 1, 1, 64, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 1, 80, fa.FA_BF16) == 0

@@ -1,0 +1,172 @@
+"""Thin Python binding of the C ABI in ``include/fa.h``.
+
+``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_main``,
+``fa_bwd_finalize``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
+the C names and argument order; pointer arguments accept an integer device
+address or any object with ``data_ptr()`` (a torch tensor), and ``stream`` an
+integer ``hipStream_t``, a torch stream, or ``None`` for torch's current stream.
+They return the C status code unchanged.  ``forward``/``backward`` are small
+conveniences that allocate outputs with torch and raise on a non-zero status.
+Every step of the computation runs in the HIP library; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+FA_BF16, FA_F32 = 0, 1
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(fa_status_string(status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_14_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+        L.fa_fwd.restype = I
+        L.fa_bwd_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.fa_bwd_workspace_size.restype = S
+        L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        L.fa_bwd.restype = I
+        L.fa_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, I, P, S, P]
+        L.fa_bwd_preprocess.restype = I
+        L.fa_bwd_main.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        L.fa_bwd_main.restype = I
+        L.fa_bwd_finalize.argtypes = [P, I, I, I, I, I, I, P, S, P]
+        L.fa_bwd_finalize.restype = I
+        L.fa_status_string.argtypes = [I]
+        L.fa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream) or None
+    if isinstance(s, int):
+        return s or None
+    return int(s.cuda_stream) or None
+
+
+# ------------------------------------------------------------------ C names
+def fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                        float(scale), int(bool(causal)), int(dtype), _stream(stream))
+
+
+def fa_bwd_workspace_size(B, H, Hkv, N, d, dtype) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, Hkv, N, d, int(dtype)))
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype,
+           workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                        _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                        int(bool(causal)), int(dtype), _ptr(workspace), int(workspace_bytes),
+                        _stream(stream))
+
+
+def fa_bwd_preprocess(o, dO, dq, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(dq), B, H, Hkv, N, d, int(dtype),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype,
+                workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_finalize(dq, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_finalize(_ptr(dq), B, H, Hkv, N, d, int(dtype), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------ conveniences
+def _dims(q, k):
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k/v [B, Hkv, N, d]")
+    if q.dtype == torch.bfloat16:
+        dt = FA_BF16
+    elif q.dtype == torch.float32:
+        dt = FA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    return B, H, k.shape[1], N, d, dt
+
+
+def _check_tensors(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def workspace(B, H, Hkv, N, d, dtype, device):
+    """A caller-owned workspace tensor and its 256-byte-aligned address and size."""
+    import torch
+    n = fa_bwd_workspace_size(B, H, Hkv, N, d, dtype)
+    if n == 0:
+        raise FAError(FA_ERR_INVALID_ARG)
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    addr = (buf.data_ptr() + 255) // 256 * 256
+    return buf, addr, n
+
+
+def forward(q, k, v, scale=None, causal=False, stream=None):
+    """(o, lse) for q [B,H,N,d], k/v [B,Hkv,N,d] (bf16 or f32 device tensors)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, Hkv, N, d, dt = _dims(q, k)
+    s = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, s, causal, dt, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None, ws=None):
+    """(dq, dk, dv) of sum(do * o); ``ws`` may pass a workspace from :func:`workspace`."""
+    import torch
+    _check_tensors(q, k, v, o, do, lse)
+    B, H, Hkv, N, d, dt = _dims(q, k)
+    s = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dv = torch.empty_like(v)
+    if ws is None:
+        ws = workspace(B, H, Hkv, N, d, dt, q.device)
+    _, addr, n = ws
+    st = fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, N, d, s, causal, dt, addr, n, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv
