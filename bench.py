@@ -3,7 +3,7 @@
 
 One step is one pass of the whole path on one batch of synthetic input that is
 already resident in HBM: ``fa_fwd`` followed by the three backward phases
-(``fa_bwd_preprocess``, ``fa_bwd_main``, ``fa_bwd_finalize``, i.e. ``fa_bwd``),
+(``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_bwd_dq``, i.e. ``fa_bwd``),
 all on one stream.  W untimed warm-up steps, then exactly K timed steps
 bracketed by ``torch.cuda.synchronize()``.  Prints ONE JSON line on stdout.
 
@@ -31,8 +31,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_bwd_main_llama2_7b_causal_n4096_d128.json")
-KERNEL_SOURCES = ["tiled_attention_14_amd/csrc/fa_bwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"]
+KERNEL_SOURCES = {"fa_fwd": ["tiled_attention_14_amd/csrc/fa_fwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"],
+                  "fa_bwd_dkdv": ["tiled_attention_14_amd/csrc/fa_bwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"],
+                  "fa_bwd_dq": ["tiled_attention_14_amd/csrc/fa_bwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"]}
 
 
 def log(*a):
@@ -52,15 +53,17 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def traffic_for_current_kernel():
-    """HBM bytes per launch of the backward main kernel from the committed
-    counter summary, or None when it is missing or the kernel source changed."""
+def traffic_for_current_kernel(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of the
+    headline workload, or None when it is missing or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_llama2_7b_causal_n4096_d128.json")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_hash") != source_hash(KERNEL_SOURCES):
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return t.get("bytes_per_launch")
 
@@ -150,11 +153,11 @@ def main():
         if ev is not None: ev[0].record(stream)
         st = fa.fa_fwd(q, k, v, o, lse, *sargs, w.scale, w.causal, dt, stream)
         if ev is not None: ev[1].record(stream)
-        st |= fa.fa_bwd_preprocess(o, do, dq, *sargs, dt, ws, ws_n, stream)
+        st |= fa.fa_bwd_preprocess(o, do, lse, *sargs, dt, ws, ws_n, stream)
         if ev is not None: ev[2].record(stream)
-        st |= fa.fa_bwd_main(q, k, v, do, lse, dq, dk, dv, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
+        st |= fa.fa_bwd_dkdv(q, k, v, do, dk, dv, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
         if ev is not None: ev[3].record(stream)
-        st |= fa.fa_bwd_finalize(dq, *sargs, dt, ws, ws_n, stream)
+        st |= fa.fa_bwd_dq(q, k, v, do, dq, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
         if ev is not None: ev[4].record(stream)
         if st != fa.FA_OK:
             raise RuntimeError("attention call failed")
@@ -173,33 +176,38 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] {args.steps} timed steps: {wall * 1e3 / args.steps:.3f} ms/step")
 
-    # Per-kernel durations: the same K steps again with events between the kernels.
+    # Per-kernel durations: the same K steps again with events between the kernels,
+    # recorded on the stream the kernels are launched on.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    names = ["fa_fwd_kernel", "fa_bwd_pre_kernel", "fa_bwd_main_kernel", "fa_bwd_dq_cvt_kernel"]
+    names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq"]
     per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
     log("[bench] kernel averages (ms): " + ", ".join(f"{n}={t:.4f}" for n, t in per.items()))
 
     f_fwd, f_bwd, f_tot = flops(w)
     ms = wall * 1e3 / args.steps
     value = f_tot / (ms * 1e-3) / 1e12
-    t_fwd = per["fa_fwd_kernel"]
-    t_bwd = per["fa_bwd_pre_kernel"] + per["fa_bwd_main_kernel"] + per["fa_bwd_dq_cvt_kernel"]
+    t_fwd = per["fa_fwd"]
+    t_bwd = per["fa_bwd_pre"] + per["fa_bwd_dkdv"] + per["fa_bwd_dq"]
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
 
-    # Dominant kernel: the backward main kernel carries all five products of the
-    # backward pass (S recompute, dP, dV, dK, dQ), i.e. F_bwd.
-    dom = max(("fa_fwd_kernel", "fa_bwd_main_kernel"), key=lambda n: per[n])
-    dom_flops = f_fwd if dom == "fa_fwd_kernel" else f_bwd
-    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
-    traffic = traffic_for_current_kernel() if (dom == "fa_bwd_main_kernel" and w.name == synth.HEADLINE) else None
+    # Algorithmic flops per kernel, in units of one N x N x d product (F_fwd / 2):
+    # the forward does 2 (S, P V); the backward's 5 (S, dP, dV, dK, dQ) split into
+    # 4 in the dK/dV kernel and 1 in the dQ kernel, whose recomputation of S and
+    # dP is not credited.  Executed products: fwd 2, dK/dV 4, dQ 3.
+    unit = f_fwd / 2
+    algo = {"fa_fwd": 2 * unit, "fa_bwd_dkdv": 4 * unit, "fa_bwd_dq": 1 * unit}
+    executed = {"fa_fwd": 2 * unit, "fa_bwd_dkdv": 4 * unit, "fa_bwd_dq": 3 * unit}
+    dom = max(algo, key=lambda n: per[n])
+    achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
+    traffic = traffic_for_current_kernel(dom) if w.name == synth.HEADLINE else None
 
-    # The preprocess is bound by HBM: it reads O and dO and writes D and the zeroed dQ accumulator.
+    # The preprocess is bound by HBM: it reads O, dO and LSE and writes D and LSE*log2(e).
     el = 2 if w.dtype == "bf16" else 4
-    pre_bytes = 2 * w.B * w.H * w.N * w.d * el + 4 * w.B * w.H * w.N + (4 * w.B * w.H * w.N * w.d)
+    pre_bytes = 2 * w.B * w.H * w.N * w.d * el + 3 * 4 * w.B * w.H * w.N
     out = {
         "metric": "attention fwd+bwd TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
         "value": round(value, 2),
@@ -221,7 +229,8 @@ def main():
         "fwd_ms": round(t_fwd, 4),
         "bwd_ms": round(t_bwd, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
-        "bwd_preprocess_gbs": round(pre_bytes / (per["fa_bwd_pre_kernel"] * 1e-3) / 1e9, 1),
+        "kernel_mfma_tflops_executed": {n: round(f / (per[n] * 1e-3) / 1e12, 2) for n, f in executed.items()},
+        "bwd_preprocess_gbs": round(pre_bytes / (per["fa_bwd_pre"] * 1e-3) / 1e9, 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }

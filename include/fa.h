@@ -29,7 +29,8 @@
  *    H must be a multiple of Hkv.  Hkv == H is ordinary multi-head attention.
  *  - `causal` != 0 applies the square causal mask: key j is visible to query i
  *    iff j <= i.
- *  - d must be 64 or 128.  N may be any value >= 1 (ragged tails are masked).
+ *  - d must be 64 or 128.  N may be any value >= 1 (ragged tails are masked);
+ *    one head's N x d slab must stay below 2 GiB.
  *  - `scale` multiplies Q K^T (typically 1/sqrt(d)); it must be finite and > 0.
  *  - lse[b,h,i] is the natural-log log-sum-exp of the scaled, masked scores of
  *    query row i.
@@ -77,20 +78,25 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    float scale, int causal, fa_dtype_t dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: one float32 per
- * query row (D_i = sum_c dO_ic * O_ic) plus, for FA_BF16, a float32 dQ
- * accumulator [B, H, N, d].  O(N) in the sequence length.  Returns 0 when the
- * sizes are invalid.
+ * Bytes of device workspace fa_bwd needs for these sizes: two float32 per
+ * query row (D_i = sum_c dO_ic * O_ic and lse_i * log2 e) and, only for GQA
+ * shapes whose query heads are spread over several workgroups of the dK/dV
+ * kernel, float32 partial sums of dK and dV (at most 8 * B * H * N * d
+ * bytes).  Linear in the sequence length N.  Valid for both values of
+ * `causal`.  Returns 0 when the sizes are invalid.
  */
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype);
 
 /*
- * Backward pass of L = sum(dO * O) for the forward above.  Inputs q, k, v, the
- * forward's o and lse, and dO; outputs dq, dk, dv (same dtype and layout as
- * q, k, v).  dk and dv sum over the query heads of each GQA group.  `workspace`
- * is device memory of at least fa_bwd_workspace_size(...) bytes, 256-byte
- * aligned, owned by the caller and not touched by anything else until the
- * enqueued work has finished; its contents on entry do not matter.
+ * Backward pass of L = sum(dO * O) for the forward above (the FlashAttention-2
+ * backward of "FlashAttention V2深度解析：反向传播显存优化让大模型训练不再OOM",
+ * section 改进1：IO感知的算子调度: P is recomputed from q, k and lse, never
+ * read from memory).  Inputs q, k, v, the forward's o and lse, and dO; outputs
+ * dq, dk, dv (same dtype and layout as q, k, v).  dk and dv sum over the query
+ * heads of each GQA group.  `workspace` is device memory of at least
+ * fa_bwd_workspace_size(...) bytes, 256-byte aligned, owned by the caller and
+ * not touched by anything else until the enqueued work has finished; its
+ * contents on entry do not matter.  Results are deterministic (no atomics).
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    const void* o, const void* dO, const float* lse,
@@ -101,32 +107,33 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
 
 /*
  * The three phases of fa_bwd, callable one by one (same arguments, layouts,
- * workspace and error rules as fa_bwd); enqueued in this order on one stream
- * they do exactly what fa_bwd does.  They exist so that callers and
- * benchmarks can time or schedule the phases separately.
+ * workspace and error rules as fa_bwd); enqueued on one stream as
+ * preprocess, then dkdv and dq (in either order) they do exactly what fa_bwd
+ * does.  They exist so that callers and benchmarks can time or schedule the
+ * phases separately.
  *
- * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic into the workspace, and zeroes
- *   the float32 dQ accumulator (the workspace for FA_BF16, dq itself for
- *   FA_F32).  Reads o and dO.
- * fa_bwd_main: recomputes P from q, k and lse and accumulates dV = P^T dO,
- *   dK = scale dS^T q and scale dS k into the dQ accumulator, with
- *   dS = P * (dO v^T - D).  Writes dk and dv; needs the preprocess first.
- * fa_bwd_finalize: FA_BF16 converts the dQ accumulator into dq; FA_F32 does
- *   nothing (dq already holds the result).
+ * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic and lse_i * log2 e into the
+ *   workspace.  Reads o, dO and lse.
+ * fa_bwd_dkdv: recomputes P = exp(scale q k^T - lse) and dS = P * (dO v^T - D)
+ *   and writes dv = P^T dO and dk = scale dS^T q.  Needs the preprocess.
+ * fa_bwd_dq: recomputes P and dS the same way and writes dq = scale dS k.
+ *   Needs the preprocess.
  */
-fa_status_t fa_bwd_preprocess(const void* o, const void* dO, void* dq,
+fa_status_t fa_bwd_preprocess(const void* o, const void* dO, const float* lse,
                               int B, int H, int Hkv, int N, int d, fa_dtype_t dtype,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-fa_status_t fa_bwd_main(const void* q, const void* k, const void* v,
-                        const void* dO, const float* lse,
-                        void* dq, void* dk, void* dv,
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                        void* dk, void* dv,
                         int B, int H, int Hkv, int N, int d,
                         float scale, int causal, fa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-fa_status_t fa_bwd_finalize(void* dq, int B, int H, int Hkv, int N, int d, fa_dtype_t dtype,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                      void* dq,
+                      int B, int H, int Hkv, int N, int d,
+                      float scale, int causal, fa_dtype_t dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status_t s);

@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_finalize", "fa_bwd_main", "fa_bwd_preprocess", "fa_bwd_workspace_size",
+    assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess", "fa_bwd_workspace_size",
                      "fa_fwd", "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
@@ -69,21 +69,21 @@ def _pre(**kw):
                                 a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
 
 
-def _main(**kw):
+def _dkdv(**kw):
     a = dict(GOOD); a.update(kw)
-    ptrs = a.pop("ptrs", [P] * 8)
-    return fa.fa_bwd_main(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+    ptrs = a.pop("ptrs", [P] * 6)
+    return fa.fa_bwd_dkdv(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
                           a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
 
 
-def _fin(**kw):
+def _dq(**kw):
     a = dict(GOOD); a.update(kw)
-    ptrs = a.pop("ptrs", [P])
-    return fa.fa_bwd_finalize(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["dtype"],
-                              a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
+    ptrs = a.pop("ptrs", [P] * 5)
+    return fa.fa_bwd_dq(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                        a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
 
 
-@pytest.mark.parametrize("call", [_fwd, _bwd, _main])
+@pytest.mark.parametrize("call", [_fwd, _bwd, _dkdv, _dq])
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), fa.FA_ERR_INVALID_ARG),
     (dict(H=0), fa.FA_ERR_INVALID_ARG),
@@ -123,7 +123,7 @@ def test_bwd_null_and_misaligned_pointers(lib, i):
     assert _bwd(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("call", [_pre, _fin])
+@pytest.mark.parametrize("call", [_pre, _dkdv, _dq])
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), fa.FA_ERR_INVALID_ARG), (dict(N=0), fa.FA_ERR_INVALID_ARG),
     (dict(H=6, Hkv=4), fa.FA_ERR_INVALID_ARG), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
@@ -134,7 +134,7 @@ def test_phase_invalid_arguments(lib, call, kw, status):
     assert call(**kw) == status
 
 
-@pytest.mark.parametrize("call,n", [(_pre, 3), (_main, 8), (_fin, 1)])
+@pytest.mark.parametrize("call,n", [(_pre, 3), (_dkdv, 6), (_dq, 5)])
 def test_phase_null_and_misaligned_pointers(lib, call, n):
     for i in range(n):
         ptrs = [P] * n
@@ -152,16 +152,22 @@ def test_workspace_errors(lib):
 
 
 def test_workspace_size_is_linear_in_n(lib):
-    for dt, per_row in ((fa.FA_BF16, lambda d: 4 * (1 + d)), (fa.FA_F32, lambda d: 4)):
+    """Two floats per query row, plus (GQA only) float32 partial dK/dV of at most
+    8 B H N d bytes: O(N) extra memory, never O(N^2)."""
+    for dt in (fa.FA_BF16, fa.FA_F32):
         for (B, H, Hkv, N, d) in [(1, 1, 1, 1, 64), (2, 32, 32, 4096, 128), (1, 64, 8, 8192, 128),
-                                  (1, 8, 8, 65536, 128), (3, 4, 2, 129, 64)]:
+                                  (1, 8, 8, 65536, 128), (3, 4, 2, 129, 64), (1, 64, 1, 4096, 128)]:
             n = fa.fa_bwd_workspace_size(B, H, Hkv, N, d, dt)
             rows = B * H * N
-            exact = per_row(d) * rows
-            assert exact <= n <= exact + 256, (dt, B, H, N, d, n)
-    # O(N): doubling N doubles the workspace (up to alignment padding), never quadruples it.
-    a = fa.fa_bwd_workspace_size(1, 8, 8, 32768, 128, fa.FA_BF16)
-    b = fa.fa_bwd_workspace_size(1, 8, 8, 65536, 128, fa.FA_BF16)
-    assert abs(b - 2 * a) <= 512
+            assert 8 * rows <= n <= 8 * rows * (1 + d) + 512, (dt, B, H, N, d, n)
+            if H == Hkv:
+                assert n <= 8 * rows + 512, (dt, B, H, N, d, n)
+    # The named multi-head shapes need nothing beyond the two row statistics.
+    assert fa.fa_bwd_workspace_size(2, 32, 32, 4096, 128, fa.FA_BF16) == 2 * 4 * 2 * 32 * 4096
+    # O(N): doubling N at most doubles the workspace (up to alignment padding).
+    for (H, Hkv) in ((8, 8), (64, 8), (16, 1)):
+        a = fa.fa_bwd_workspace_size(1, H, Hkv, 32768, 128, fa.FA_BF16)
+        b = fa.fa_bwd_workspace_size(1, H, Hkv, 65536, 128, fa.FA_BF16)
+        assert b <= 2 * a + 512, (H, Hkv, a, b)
     assert fa.fa_bwd_workspace_size(0, 1, 1, 1, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 1, 1, 80, fa.FA_BF16) == 0

@@ -2,6 +2,7 @@
 // layout and kernel dispatch.  Nothing here allocates, prints or throws.
 #include "../../include/fa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -10,59 +11,90 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+// Compute units of one MI355X; only used to balance the dK/dV work split.
+constexpr double kCUs = 256.0;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shared shape checks.  Element counts must fit comfortably in 63 bits and
-// every per-tensor count must stay below 2^40 elements.
+// Shared shape checks.  Every per-head slab (N x d elements) must stay below
+// 2^31 bytes (32-bit buffer offsets) and grids must fit 32 bits.
 fa_status_t check_shape(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype, float scale) {
   if (B < 1 || H < 1 || Hkv < 1 || N < 1) return FA_ERR_INVALID_ARG;
   if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const double elems = (double)B * H * N * d;
-  if (elems >= 1099511627776.0) return FA_ERR_INVALID_ARG;
-  // Grid sizes are 32-bit: (query or key tiles) x B x H must fit.
+  const double esize = dtype == FA_BF16 ? 2.0 : 4.0;
+  if ((double)(N + 256) * d * esize >= 2147483648.0) return FA_ERR_INVALID_ARG;
+  if ((double)B * H * N * d >= 1099511627776.0) return FA_ERR_INVALID_ARG;
   if ((double)B * H * ((N + 31) / 32) >= 2147483647.0) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
+// Number of workgroups a GQA group's query heads are spread over in the dK/dV
+// kernel.  One workgroup per (batch, KV head, key tile) loops over all g query
+// heads; when that makes the heaviest workgroup much longer than the average
+// work per compute unit, or leaves compute units idle, the heads are sliced
+// and the slices' float32 partial sums are reduced afterwards.
+int dkdv_nsplit(int B, int H, int Hkv, int N, bool causal) {
+  const int g = H / Hkv;
+  if (g == 1) return 1;
+  const long nkt = (N + fa::kDkdvKeys - 1) / fa::kDkdvKeys;
+  const long nq = (N + fa::kDkdvQRows - 1) / fa::kDkdvQRows;
+  const long step = fa::kDkdvKeys / fa::kDkdvQRows;      // query tiles per key tile
+  const long first = nq;                                  // steps of key tile 0, per head
+  const long sum = causal ? nkt * nq - step * nkt * (nkt - 1) / 2 : nkt * nq;
+  const double avg = (double)B * Hkv * g * sum / kCUs;    // steps per compute unit
+  for (int ns = 1; ns < g; ++ns) {
+    if (g % ns) continue;
+    const double heavy = (double)(g / ns) * first;
+    const double units = (double)B * Hkv * nkt * ns;
+    if (heavy <= 1.25 * avg && units >= 2.0 * kCUs) return ns;
+  }
+  return g;
+}
+
 struct WorkspaceLayout {
-  size_t delta_off, delta_bytes, dq_off, dq_bytes, total;
+  size_t delta_off, lse2_off, part_off, total;
 };
 
-WorkspaceLayout layout(int B, int H, int N, int d, fa_dtype_t dtype) {
+WorkspaceLayout layout(int B, int H, int Hkv, int N, int d, int nsplit) {
   WorkspaceLayout w;
   const size_t rows = (size_t)B * H * N;
   w.delta_off = 0;
-  w.delta_bytes = rows * sizeof(float);
-  w.dq_off = round_up(w.delta_bytes, kAlign);
-  w.dq_bytes = dtype == FA_BF16 ? rows * d * sizeof(float) : 0;
-  w.total = w.dq_off + w.dq_bytes;
+  w.lse2_off = round_up(rows * sizeof(float), kAlign);
+  w.part_off = w.lse2_off + round_up(rows * sizeof(float), kAlign);
+  const size_t part = nsplit > 1 ? 2 * (size_t)nsplit * B * Hkv * N * d * sizeof(float) : 0;
+  w.total = w.part_off + part;
   return w;
 }
 
-// Validates the shared backward arguments and fills the shape, workspace and
-// accumulator fields of p.
+// Validates the shared backward arguments and fills the shape and workspace fields of p.
 fa_status_t bwd_params(int B, int H, int Hkv, int N, int d, float scale, int causal, fa_dtype_t dtype,
-                       void* workspace, size_t workspace_bytes, void* dq, fa::BwdParams* p) {
+                       void* workspace, size_t workspace_bytes, fa::BwdParams* p) {
   fa_status_t st = check_shape(B, H, Hkv, N, d, dtype, scale);
   if (st != FA_OK) return st;
-  const WorkspaceLayout wl = layout(B, H, N, d, dtype);
+  *p = fa::BwdParams{};
+  p->nsplit = dkdv_nsplit(B, H, Hkv, N, causal != 0);
+  const WorkspaceLayout wl = layout(B, H, Hkv, N, d, p->nsplit);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < wl.total)
     return FA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  *p = fa::BwdParams{};
-  p->dq = dq;
   p->delta = reinterpret_cast<float*>(ws + wl.delta_off);
-  p->dq_acc = dtype == FA_BF16 ? reinterpret_cast<float*>(ws + wl.dq_off) : static_cast<float*>(dq);
+  p->lse2 = reinterpret_cast<float*>(ws + wl.lse2_off);
+  p->part = p->nsplit > 1 ? reinterpret_cast<float*>(ws + wl.part_off) : nullptr;
   p->B = B; p->H = H; p->Hkv = Hkv; p->N = N; p->d = d;
   p->scale = scale; p->causal = causal != 0;
   p->dtype = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
   return FA_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!x || !aligned16(x)) return false;
+  return true;
 }
 
 }  // namespace
@@ -71,8 +103,7 @@ extern "C" {
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
                    int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
   fa_status_t st = check_shape(B, H, Hkv, N, d, dtype, scale);
   if (st != FA_OK) return st;
   fa::FwdParams p;
@@ -85,57 +116,53 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype) {
   if (check_shape(B, H, Hkv, N, d, dtype, 1.0f) != FA_OK) return 0;
-  return layout(B, H, N, d, dtype).total;
+  const int ns = std::max(dkdv_nsplit(B, H, Hkv, N, false), dkdv_nsplit(B, H, Hkv, N, true));
+  return layout(B, H, Hkv, N, d, ns).total;
 }
 
-fa_status_t fa_bwd_preprocess(const void* o, const void* dO, void* dq, int B, int H, int Hkv, int N, int d,
+fa_status_t fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int Hkv, int N, int d,
                               fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!o || !dO || !dq) return FA_ERR_INVALID_ARG;
-  if (!aligned16(o) || !aligned16(dO) || !aligned16(dq)) return FA_ERR_INVALID_ARG;
+  if (!all_aligned({o, dO, lse})) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
-  fa_status_t st = bwd_params(B, H, Hkv, N, d, 1.0f, 0, dtype, workspace, workspace_bytes, dq, &p);
+  fa_status_t st = bwd_params(B, H, Hkv, N, d, 1.0f, 0, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
-  p.o = o; p.dO = dO;
+  p.o = o; p.dO = dO; p.lse = lse;
   return fa::launch_bwd_pre(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
-                        void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
-                        fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_INVALID_ARG;
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv, int B,
+                        int H, int Hkv, int N, int d, float scale, int causal, fa_dtype_t dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (!all_aligned({q, k, v, dO, dk, dv})) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
-  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, dq, &p);
+  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
-  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.dk = dk; p.dv = dv;
-  return fa::launch_bwd_main(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.dk = dk; p.dv = dv;
+  return fa::launch_bwd_dkdv(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_bwd_finalize(void* dq, int B, int H, int Hkv, int N, int d, fa_dtype_t dtype, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
-  if (!dq || !aligned16(dq)) return FA_ERR_INVALID_ARG;
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H, int Hkv,
+                      int N, int d, float scale, int causal, fa_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!all_aligned({q, k, v, dO, dq})) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
-  fa_status_t st = bwd_params(B, H, Hkv, N, d, 1.0f, 0, dtype, workspace, workspace_bytes, dq, &p);
+  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
-  return fa::launch_bwd_finalize(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.dq = dq;
+  return fa::launch_bwd_dq(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                    void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
                    fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, o, dO, lse, dq, dk, dv})) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
-  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, dq, &p);
+  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
-  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dk = dk; p.dv = dv;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
   if (fa::launch_bwd_pre(p, stream) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_main(p, stream) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_finalize(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

@@ -16,26 +16,58 @@
 // row constant D equals sum_j P_ij dP_ij because O = P V.
 //
 // Kernels (all on the caller's stream, no host synchronisation):
-//  1. fa_bwd_pre:  D = rowsum(dO * O) and zeroing of the fp32 dQ accumulator;
-//  2. fa_bwd_main: one workgroup per (batch, KV head, 128-key tile); K/V stay
-//     resident in registers, dK/dV accumulate in registers (no atomics); the
-//     workgroup walks the query tiles of every query head of its GQA group
-//     (only tiles at or after the diagonal under the causal mask) and adds
-//     its share of dQ into the fp32 accumulator with hardware float atomics;
-//  3. fa_bwd_dq_cvt: dQ accumulator -> bf16 (the f32 path accumulates into dq
-//     directly and skips it).
+//  1. fa_bwd_pre:  D = rowsum(dO * O) and lse * log2(e), one float each per
+//     query row, into the workspace;
+//  2. fa_bwd_dkdv: one workgroup per (batch, KV head, 128-key tile[, slice of
+//     the GQA group]); K/V fragments and the dK/dV accumulators stay in
+//     registers while Q/dO tiles of 64 rows stream through LDS (global -> LDS
+//     copies, double-buffered), for every query head of the group and, under
+//     the causal mask, only from the diagonal on.  No atomics: each key row is
+//     owned by one lane.  When a GQA group is sliced over several workgroups
+//     (to balance the work of very wide groups), each writes float32 partial
+//     sums and fa_bwd_reduce adds them in a fixed order;
+//  3. fa_bwd_dq:   one workgroup per (batch, head, 128-query tile); Q/dO
+//     fragments and the dQ accumulator stay in registers while K/V tiles of 64
+//     keys stream through LDS.  It recomputes S and dP instead of exchanging
+//     dS with the dK/dV kernel: seven products in total instead of five, but
+//     no float atomics, whose L2 throughput on this part is far below what a
+//     shared dQ accumulator would need.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* dO;
+  const float* delta; const float* lse2;
+  void* dq; void* dk; void* dv;
+  float* part;
+  int B, H, Hkv, N, nsplit;
+  float c;      // scale * log2(e)
+  float scale;
+};
+
+BwdArgs make_args(const BwdParams& p) {
+  BwdArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.dO = p.dO;
+  a.delta = p.delta; a.lse2 = p.lse2;
+  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.part = p.part;
+  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N; a.nsplit = p.nsplit;
+  a.c = p.scale * kLog2e;
+  a.scale = p.scale;
+  return a;
+}
+
 // ------------------------------------------------------------------ 1. preprocess
-// One thread per 8 elements of a row; D/8 threads share a row.
+// D/8 threads share a row; each handles 8 elements.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                         float* __restrict__ delta, float* __restrict__ dq_acc,
-                                                         long rows) {
+                                                         const float* __restrict__ lse, float* __restrict__ delta,
+                                                         float* __restrict__ lse2, long rows) {
   constexpr int TPR = D / 8;
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = t / TPR;
@@ -45,270 +77,373 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const T* __restrict__ O
     const size_t off = (size_t)row * D + c8 * 8;
     float o[8], g[8];
     if constexpr (sizeof(T) == 2) {
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(O + off);
-      bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + off);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(O + off);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(dO + off);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { o[i] = (float)a[i]; g[i] = (float)b[i]; }
+      for (int i = 0; i < 8; ++i) { o[i] = (float)x[i]; g[i] = (float)y[i]; }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) { o[i] = O[off + i]; g[i] = dO[off + i]; }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(o[i], g[i], acc);
-    f32x4* z = reinterpret_cast<f32x4*>(dq_acc + off);
-    z[0] = f32x4{};
-    z[1] = f32x4{};
   }
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, TPR);
-  if (row < rows && c8 == 0) delta[row] = acc;
+  if (row < rows && c8 == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
-// ------------------------------------------------------------------ 3. dQ convert
-__global__ __launch_bounds__(256) void fa_bwd_dq_cvt_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                            long n8) {
-  const long t = (long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n8) return;
-  const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * t];
-  const f32x4 b = reinterpret_cast<const f32x4*>(acc)[2 * t + 1];
-  reinterpret_cast<bf16x8*>(dq)[t] =
-      bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-}
+// ------------------------------------------------------------------ 2. dK / dV
+constexpr int kKeys = kDkdvKeys;    // keys per workgroup (32 per wave)
+constexpr int kQRows = kDkdvQRows;  // query rows per step
+static_assert(kKeys == 32 * kWaves, "one 32-key column block per wave");
 
-// ------------------------------------------------------------------ 2. main
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kBwdBc = 32 * kBwdWaves;  // keys per workgroup
-
-struct BwdArgs {
-  const void* q; const void* k; const void* v; const void* dO;
-  const float* lse; const float* delta;
-  float* dq_acc; void* dk; void* dv;
-  int B, H, Hkv, N, nkt;
-  float c;      // scale * log2(e)
-  float scale;
-};
-
-// MB = number of 32-row query blocks per inner step (query tile = 32*MB rows).
-template <typename T, int D, bool CAUSAL, int MB>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_main_kernel(BwdArgs a) {
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   typedef typename Frag<T>::type F;
-  constexpr int BR = 32 * MB;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int QST = D + EPC;       // Q / dO tile row stride
-  constexpr int KST = D + 2 * EPC;   // K tile row stride
-  constexpr int SST = BR + 4;       // dS^T tile row stride (keeps 16 B alignment for f32 rows)
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) T sQ[BR * QST];
-  __shared__ __attribute__((aligned(16))) T sdO[BR * QST];
-  __shared__ __attribute__((aligned(16))) T sK[kBwdBc * KST];
-  __shared__ __attribute__((aligned(16))) T sdS[kBwdBc * SST];
-  __shared__ float sL[BR], sD[BR];
+  typedef Lay<T, D> L;
+  constexpr int TB = kQRows * L::RB;
+  constexpr int KS = D / 16, DB = D / 32, MB = kQRows / 32;
+  __shared__ __attribute__((aligned(1024))) char sQ0[TB], sQ1[TB], sO0[TB], sO1[TB];
+  __shared__ __attribute__((aligned(256))) float sL0[kQRows], sL1[kQRows], sD0[kQRows], sD1[kQRows];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = a.N;
-  const int BHkv = a.B * a.Hkv;
-  const int kt = blockIdx.x / BHkv;          // lowest key tiles carry the most work: first
-  const int bkv = blockIdx.x % BHkv;
+  const int g = a.H / a.Hkv, gs = g / a.nsplit;
+  int unit, kt;
+  xcd_map(blockIdx.x, a.B * a.Hkv * a.nsplit, unit, kt);  // lowest key tiles (most work) first
+  const int bkv = unit / a.nsplit, sp = unit % a.nsplit;
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
-  const int g = a.H / a.Hkv;
-  const int k0 = kt * kBwdBc;
-  const int kw = k0 + 32 * w;                // first key of this wave
-  const int mykey = kw + l32;                // key column owned by this lane
-
-  const T* K = reinterpret_cast<const T*>(a.k) + (size_t)bkv * N * D;
-  const T* V = reinterpret_cast<const T*>(a.v) + (size_t)bkv * N * D;
+  const int h0 = kvh * g + sp * gs;  // first query head of this slice
+  const size_t slab = (size_t)N * D;
+  const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
+  const int k0 = kt * kKeys;
+  const int kw = k0 + 32 * w;  // first key of this wave
+  const int mykey = kw + l32;  // key row owned by this lane
 
   // K and V rows of this lane's key, as B fragments of S = Q K^T and dP = dO V^T.
   F kf[KS], vf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (mykey < N) {
-      frag_rm(kf[s], K + (size_t)mykey * D + 16 * s + 8 * hf);
-      frag_rm(vf[s], V + (size_t)mykey * D + 16 * s + 8 * hf);
-    } else {
-      frag_zero(kf[s]);
-      frag_zero(vf[s]);
-    }
-  }
   {
-    TileCopy<T, kBwdBc, D, KST, kBwdThreads> kc;
-    kc.load(K, k0, N, tid);
-    kc.store(sK, tid);
+    const rsrc_t rK = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)bkv * slab, slab_bytes);
+    const rsrc_t rV = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)bkv * slab, slab_bytes);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag_global<D>(kf[s], rK, mykey, 16 * s + 8 * hf);
+      frag_global<D>(vf[s], rV, mykey, 16 * s + 8 * hf);
+    }
   }
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  const int nqt = (N + BR - 1) / BR;
-  const int qstart = CAUSAL ? k0 / BR : 0;
+  const int nqt = (N + kQRows - 1) / kQRows;
+  const int qstart = CAUSAL ? k0 / kQRows : 0;
   const int nq = nqt - qstart;
-  const int total = g * nq;
+  const int total = gs * nq;
 
-  TileCopy<T, BR, D, QST, kBwdThreads> qc, oc;
-  float stat = 0.f;  // threads [0, BR): LSE (log2 units); [BR, 2 BR): D
-  auto fetch = [&](int it) {
-    const int hq = kvh * g + it / nq;
-    const int qb0 = (qstart + it % nq) * BR;
-    const size_t base = ((size_t)b * a.H + hq) * N;
-    qc.load(reinterpret_cast<const T*>(a.q) + base * D, qb0, N, tid);
-    oc.load(reinterpret_cast<const T*>(a.dO) + base * D, qb0, N, tid);
-    if (tid < BR) stat = (qb0 + tid < N) ? a.lse[base + qb0 + tid] * kLog2e : 0.f;
-    else if (tid < 2 * BR) stat = (qb0 + tid - BR < N) ? a.delta[base + qb0 + tid - BR] : 0.f;
-  };
-  auto stage = [&]() {
-    qc.store(sQ, tid);
-    oc.store(sdO, tid);
-    if (tid < BR) sL[tid] = stat;
-    else if (tid < 2 * BR) sD[tid - BR] = stat;
-  };
-
-  if (total > 0) {
-    fetch(0);
-    stage();
-  }
+  lds_zero<kThreads>(sQ0, TB); lds_zero<kThreads>(sQ1, TB);
+  lds_zero<kThreads>(sO0, TB); lds_zero<kThreads>(sO1, TB);
+  lds_zero<kThreads>(reinterpret_cast<char*>(sL0), 4 * kQRows);
+  lds_zero<kThreads>(reinterpret_cast<char*>(sL1), 4 * kQRows);
+  lds_zero<kThreads>(reinterpret_cast<char*>(sD0), 4 * kQRows);
+  lds_zero<kThreads>(reinterpret_cast<char*>(sD1), 4 * kQRows);
   __syncthreads();
 
-  for (int it = 0; it < total; ++it) {
-    const int hq = kvh * g + it / nq;
-    const int qb0 = (qstart + it % nq) * BR;
-    if (it + 1 < total) fetch(it + 1);
+  // Copies of step `it` (query head h0 + it / nq, query tile qstart + it % nq).
+  auto fetch = [&](int it, char* bq, char* bo, float* bl, float* bd) {
+    const int hq = h0 + it / nq;
+    const int qb0 = (qstart + it % nq) * kQRows;
+    const size_t head = (size_t)b * a.H + hq;
+    const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + head * slab, slab_bytes);
+    const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.dO) + head * slab, slab_bytes);
+    tile_to_lds<T, D, kQRows, kWaves>(rQ, bq, qb0, w);
+    tile_to_lds<T, D, kQRows, kWaves>(rO, bo, qb0, w);
+    if (w == 0) vec64_to_lds(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
+    if (w == 1) vec64_to_lds(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
+  };
 
-    const bool active = !CAUSAL || (kw <= qb0 + BR - 1);
-    T* dsrow = sdS + (32 * w + l32) * SST;
-    if (active) {
-      f32x16 s[MB], dp[MB];
+  auto step = [&](const char* sQ, const char* sO, const float* sL, const float* sD, int it) {
+    const int qb0 = (qstart + it % nq) * kQRows;
+    if (CAUSAL && qb0 + kQRows - 1 < kw) return;  // every query of the step is before every key of the wave
+    f32x16 s[MB], dp[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        s[mb] = f32x16{};
-        dp[mb] = f32x16{};
+    for (int mb = 0; mb < MB; ++mb) {
+      s[mb] = f32x16{};
+      dp[mb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          F qa, oa;
-          frag_rm(qa, sQ + (mb * 32 + l32) * QST + 16 * ks + 8 * hf);
-          frag_rm(oa, sdO + (mb * 32 + l32) * QST + 16 * ks + 8 * hf);
-          s[mb] = mfma_k16(qa, kf[ks], s[mb]);
-          dp[mb] = mfma_k16(oa, vf[ks], dp[mb]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        F qa, oa;
+        frag_row<D>(qa, sQ, mb * 32 + l32, 16 * ks + 8 * hf);
+        frag_row<D>(oa, sO, mb * 32 + l32, 16 * ks + 8 * hf);
+        s[mb] = mfma_k16(qa, kf[ks], s[mb]);
+        dp[mb] = mfma_k16(oa, vf[ks], dp[mb]);
       }
-      const bool need_mask = (kw + 31 >= N) || (qb0 + BR > N) || (CAUSAL && kw + 31 > qb0);
+    }
+    const bool need_mask = (CAUSAL && kw + 31 > qb0) || (qb0 + kQRows > N);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = mb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          float p = fast_exp2(__builtin_fmaf(s[mb][i], a.c, -sL[ql]));
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ql0 = mb * 32 + 8 * g4 + 4 * hf;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql0);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(sD + ql0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float p = fast_exp2(__builtin_fmaf(s[mb][i], a.c, -lv[e]));
           if (need_mask) {
-            const int q = qb0 + ql;
-            if (mykey >= N || q >= N || (CAUSAL && mykey > q)) p = 0.f;
+            const int q = qb0 + ql0 + e;
+            if ((CAUSAL && mykey > q) || q >= N) p = 0.f;
           }
           s[mb][i] = p;
-          dp[mb][i] = p * (dp[mb][i] - sD[ql]);
-        }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step.
-#pragma unroll
-      for (int t = 0; t < 2 * MB; ++t) {
-        F pf, dsf;
-        frag_from(pf, s[t >> 1], (t & 1) * 8);
-        frag_from(dsf, dp[t >> 1], (t & 1) * 8);
-        const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          F oa, qa;
-          frag_tr(oa, sdO, QST, rA, rA + 8, db * 32);
-          dv[db] = mfma_k16(oa, pf, dv[db]);
-          frag_tr(qa, sQ, QST, rA, rA + 8, db * 32);
-          dk[db] = mfma_k16(qa, dsf, dk[db]);
+          dp[mb][i] = p * (dp[mb][i] - dd[e]);
         }
       }
-      // scale * dS^T into LDS for the dQ product.
+    // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step.
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int t = 0; t < 2 * MB; ++t) {
+      F pf, dsf;
+      frag_from(pf, s[t >> 1], (t & 1) * 8);
+      frag_from(dsf, dp[t >> 1], (t & 1) * 8);
+      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          store4(dsrow + mb * 32 + 8 * gi + 4 * hf, a.scale * dp[mb][4 * gi], a.scale * dp[mb][4 * gi + 1],
-                 a.scale * dp[mb][4 * gi + 2], a.scale * dp[mb][4 * gi + 3]);
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) store4(dsrow + mb * 32 + 8 * gi + 4 * hf, 0.f, 0.f, 0.f, 0.f);
+      for (int db = 0; db < DB; ++db) {
+        F oa, qa;
+        frag_col<D>(oa, sO, rA, rA + 8, db * 32);
+        dv[db] = mfma_k16(oa, pf, dv[db]);
+        frag_col<D>(qa, sQ, rA, rA + 8, db * 32);
+        dk[db] = mfma_k16(qa, dsf, dk[db]);
+      }
     }
-    __syncthreads();
+  };
 
-    // dQ[BR x D] += (scale dS)[BR x 128] K[128 x D]; 32x32 output blocks over the waves.
-    {
-      float* dq = a.dq_acc + ((size_t)b * a.H + hq) * N * D;
-      for (int blk = w; blk < MB * DB; blk += kBwdWaves) {
-        const int qb = blk % MB, db = blk / MB;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int t = 0; t < kBwdBc / 16; ++t) {
-          const int rA = 16 * t + 4 * hf;
-          F sa, kb;
-          frag_tr(sa, sdS, SST, rA, rA + 8, qb * 32);
-          frag_tr(kb, sK, KST, rA, rA + 8, db * 32);
-          acc = mfma_k16(sa, kb, acc);
-        }
-        const int d = db * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qb0 + qb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (q < N) unsafeAtomicAdd(dq + (size_t)q * D + d, acc[i]);
-        }
-      }
-    }
-    if (it + 1 < total) stage();
+  if (total > 0) fetch(0, sQ0, sO0, sL0, sD0);
+  wait_copies();
+  __syncthreads();
+  for (int it = 0; it < total; it += 2) {
+    if (it + 1 < total) fetch(it + 1, sQ1, sO1, sL1, sD1);
+    step(sQ0, sO0, sL0, sD0, it);
+    wait_copies();
+    __syncthreads();
+    if (it + 1 >= total) break;
+    if (it + 2 < total) fetch(it + 2, sQ0, sO0, sL0, sD0);
+    step(sQ1, sO1, sL1, sD1, it + 1);
+    wait_copies();
     __syncthreads();
   }
 
-  if (mykey < N) {
-    T* dK = reinterpret_cast<T*>(a.dk) + (size_t)bkv * N * D + (size_t)mykey * D;
-    T* dV = reinterpret_cast<T*>(a.dv) + (size_t)bkv * N * D + (size_t)mykey * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int d = db * 32 + 8 * gi + 4 * hf;
-        store4(dK + d, a.scale * dk[db][4 * gi], a.scale * dk[db][4 * gi + 1], a.scale * dk[db][4 * gi + 2],
-               a.scale * dk[db][4 * gi + 3]);
-        store4(dV + d, dv[db][4 * gi], dv[db][4 * gi + 1], dv[db][4 * gi + 2], dv[db][4 * gi + 3]);
-      }
+  if (a.nsplit == 1) {
+    store_rows<T, D>(reinterpret_cast<T*>(a.dk) + (size_t)bkv * slab, mykey, N, dk, a.scale);
+    store_rows<T, D>(reinterpret_cast<T*>(a.dv) + (size_t)bkv * slab, mykey, N, dv, 1.f);
+  } else {
+    const size_t ps = (size_t)a.B * a.Hkv * slab;  // elements of one partial tensor
+    store_rows<float, D>(a.part + (2 * sp) * ps + (size_t)bkv * slab, mykey, N, dk, a.scale);
+    store_rows<float, D>(a.part + (2 * sp + 1) * ps + (size_t)bkv * slab, mykey, N, dv, 1.f);
   }
 }
 
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_bf16(BwdArgs a) { dkdv_body<bf16, D, CAUSAL>(a); }
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_f32(BwdArgs a) { dkdv_body<float, D, CAUSAL>(a); }
+
+// Sums the nsplit float32 partials of dK and dV (in slice order) into dk / dv.
+template <typename T>
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restrict__ part, T* __restrict__ dk,
+                                                            T* __restrict__ dv, long n4, int nsplit) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= 2 * n4) return;
+  const int which = t >= n4;  // 0: dK, 1: dV
+  const long i = t - which * n4;
+  const f32x4* p = reinterpret_cast<const f32x4*>(part) + which * n4 + i;
+  f32x4 acc = p[0];
+  for (int s = 1; s < nsplit; ++s) acc += p[(long)s * 2 * n4];
+  store4((which ? dv : dk) + 4 * i, acc[0], acc[1], acc[2], acc[3]);
+}
+
+// ------------------------------------------------------------------ 3. dQ
+constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
+constexpr int kKTile = 64;           // keys per streamed tile
+
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
+  typedef typename Frag<T>::type F;
+  typedef Lay<T, D> L;
+  constexpr int TB = kKTile * L::RB;
+  constexpr int KS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int N = a.N;
+  int bh, qi;
+  xcd_map(blockIdx.x, a.B * a.H, bh, qi);
+  const int qt = CAUSAL ? nqt - 1 - qi : qi;
+  const int b = bh / a.H, h = bh % a.H;
+  const int kvh = h / (a.H / a.Hkv);
+  const size_t slab = (size_t)N * D;
+  const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
+  const rsrc_t rK = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
+  const rsrc_t rV = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
+
+  const int q0w = qt * kQTile + 32 * w;
+  const int myq = q0w + l32;
+  F qf[KS], of[KS];
+  float l2, dd;
+  {
+    const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)bh * slab, slab_bytes);
+    const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)bh * slab, slab_bytes);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
+      frag_global<D>(of[s], rO, myq, 16 * s + 8 * hf);
+    }
+    l2 = load4f(make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
+    dd = load4f(make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
+  }
+
+  const int kend = CAUSAL ? min(N, (qt + 1) * kQTile) : N;
+  const int nt = (kend + kKTile - 1) / kKTile;
+
+  lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
+  lds_zero<kThreads>(sV0, TB); lds_zero<kThreads>(sV1, TB);
+  __syncthreads();
+  tile_to_lds<T, D, kKTile, kWaves>(rK, sK0, 0, w);
+  tile_to_lds<T, D, kKTile, kWaves>(rV, sV0, 0, w);
+  wait_copies();
+  __syncthreads();
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  auto tile = [&](const char* sK, const char* sV, int k0) {
+    if (CAUSAL && k0 > q0w + 31) return;
+    // S^T = K Q^T and dP^T = V dO^T for this wave's 32 queries.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        F kf, vf;
+        frag_row<D>(kf, sK, kb * 32 + l32, 16 * ks + 8 * hf);
+        frag_row<D>(vf, sV, kb * 32 + l32, 16 * ks + 8 * hf);
+        s[kb] = mfma_k16(kf, qf[ks], s[kb]);
+        dp[kb] = mfma_k16(vf, of[ks], dp[kb]);
+      }
+    }
+    const bool need_mask = CAUSAL ? (k0 + kKTile - 1 > q0w) : (k0 + kKTile > N);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -l2));
+        if (need_mask) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (CAUSAL ? key > myq : key >= N) p = 0.f;
+        }
+        dp[kb][i] = p * (dp[kb][i] - dd);
+      }
+    // dQ^T += K^T dS^T, 16 keys per step.
+#pragma unroll
+    for (int t = 0; t < kKTile / 16; ++t) {
+      F dsf;
+      frag_from(dsf, dp[t >> 1], (t & 1) * 8);
+      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        F kf;
+        frag_col<D>(kf, sK, rA, rA + 8, db * 32);
+        acc[db] = mfma_k16(kf, dsf, acc[db]);
+      }
+    }
+  };
+
+  for (int j = 0; j < nt; j += 2) {
+    if (j + 1 < nt) {
+      tile_to_lds<T, D, kKTile, kWaves>(rK, sK1, (j + 1) * kKTile, w);
+      tile_to_lds<T, D, kKTile, kWaves>(rV, sV1, (j + 1) * kKTile, w);
+    }
+    tile(sK0, sV0, j * kKTile);
+    wait_copies();
+    __syncthreads();
+    if (j + 1 >= nt) break;
+    if (j + 2 < nt) {
+      tile_to_lds<T, D, kKTile, kWaves>(rK, sK0, (j + 2) * kKTile, w);
+      tile_to_lds<T, D, kKTile, kWaves>(rV, sV0, (j + 2) * kKTile, w);
+    }
+    tile(sK1, sV1, (j + 1) * kKTile);
+    wait_copies();
+    __syncthreads();
+  }
+
+  store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
+  dq_body<bf16, D, CAUSAL>(a, nqt);
+}
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel_f32(BwdArgs a, int nqt) {
+  dq_body<float, D, CAUSAL>(a, nqt);
+}
+
+// ------------------------------------------------------------------ launchers
 template <typename T, int D>
 hipError_t launch_pre_t(const BwdParams& p, hipStream_t stream) {
   const long rows = (long)p.B * p.H * p.N;
   const long threads = rows * (D / 8);
   hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dO), p.delta, p.dq_acc, rows);
+                     reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dO), p.lse, p.delta, p.lse2, rows);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch_main_t(const BwdParams& p, hipStream_t stream) {
-  constexpr int MB = sizeof(T) == 2 ? 2 : 1;
-  BwdArgs a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.dO = p.dO; a.lse = p.lse; a.delta = p.delta;
-  a.dq_acc = p.dq_acc; a.dk = p.dk; a.dv = p.dv;
-  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N;
-  a.nkt = (p.N + kBwdBc - 1) / kBwdBc;
-  a.c = p.scale * kLog2e;
-  a.scale = p.scale;
-  const long grid = (long)a.nkt * p.B * p.Hkv;
-  hipLaunchKernelGGL((fa_bwd_main_kernel<T, D, CAUSAL, MB>), dim3((unsigned)grid), dim3(kBwdThreads), 0, stream, a);
+hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
+  const BwdArgs a = make_args(p);
+  const int nkt = (p.N + kKeys - 1) / kKeys;
+  const dim3 grid((unsigned)((long)nkt * p.B * p.Hkv * p.nsplit));
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const long n4 = (long)p.B * p.Hkv * p.N * D / 4;
+  hipLaunchKernelGGL((fa_bwd_reduce_kernel<T>), dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, stream,
+                     p.part, reinterpret_cast<T*>(p.dk), reinterpret_cast<T*>(p.dv), n4, p.nsplit);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_main_d(const BwdParams& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_main_t<T, 64, true>(p, s) : launch_main_t<T, 64, false>(p, s);
-  return p.causal ? launch_main_t<T, 128, true>(p, s) : launch_main_t<T, 128, false>(p, s);
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
+  const BwdArgs a = make_args(p);
+  const int nqt = (p.N + kQTile - 1) / kQTile;
+  const dim3 grid((unsigned)((long)nqt * p.B * p.H));
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a, nqt);
+  else
+    hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a, nqt);
+  return hipGetLastError();
 }
+
+#define FA_DISPATCH(fn, p, s)                                                                      \
+  do {                                                                                             \
+    if ((p).dtype == kBF16) {                                                                      \
+      if ((p).d == 64) return (p).causal ? fn<bf16, 64, true>(p, s) : fn<bf16, 64, false>(p, s);  \
+      return (p).causal ? fn<bf16, 128, true>(p, s) : fn<bf16, 128, false>(p, s);                 \
+    }                                                                                              \
+    if ((p).d == 64) return (p).causal ? fn<float, 64, true>(p, s) : fn<float, 64, false>(p, s);  \
+    return (p).causal ? fn<float, 128, true>(p, s) : fn<float, 128, false>(p, s);                 \
+  } while (0)
 
 }  // namespace
 
@@ -317,16 +452,8 @@ hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t stream) {
   return p.d == 64 ? launch_pre_t<float, 64>(p, stream) : launch_pre_t<float, 128>(p, stream);
 }
 
-hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream) {
-  return p.dtype == kBF16 ? launch_main_d<bf16>(p, stream) : launch_main_d<float>(p, stream);
-}
+hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) { FA_DISPATCH(launch_dkdv_t, p, stream); }
 
-hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t stream) {
-  if (p.dtype != kBF16) return hipSuccess;  // the f32 path accumulates into dq directly
-  const long n8 = (long)p.B * p.H * p.N * p.d / 8;
-  hipLaunchKernelGGL(fa_bwd_dq_cvt_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, p.dq_acc,
-                     reinterpret_cast<bf16*>(p.dq), n8);
-  return hipGetLastError();
-}
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) { FA_DISPATCH(launch_dq_t, p, stream); }
 
 }  // namespace fa

@@ -1,20 +1,27 @@
-// fa_device.h — gfx950 device helpers shared by the attention kernels.
+// fa_device.h — gfx950 device building blocks shared by the attention kernels.
 //
-// Matrix-core conventions used throughout (checked on gfx950 hardware):
-//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
-//     A: lane l holds row (l % 32), k = 8*(l / 32) + 0..7       (8 bf16)
-//     B: lane l holds col (l % 32), k = 8*(l / 32) + 0..7       (8 bf16)
-//     D: lane l holds col (l % 32), register i holds
-//        row 8*(i / 4) + 4*(l / 32) + (i % 4)                    (16 fp32)
-//   v_mfma_f32_32x32x2_f32 has the same D layout; A/B hold k = l / 32.
-//   ds_read_b64_tr_b16: within each group of 16 lanes, result lane j element e
-//     is element (j % 4) of the 8 bytes addressed by lane 4*e + j/4.
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, D[32x32] += A[32x16] B[16x32]):
+//   A: lane l holds row (l % 32), k = 8*(l / 32) + 0..7             (8 bf16)
+//   B: lane l holds col (l % 32), k = 8*(l / 32) + 0..7             (8 bf16)
+//   D: lane l holds col (l % 32); register i holds
+//      row 8*(i / 4) + 4*(l / 32) + (i % 4)                          (16 fp32)
+// v_mfma_f32_32x32x2_f32 has the same D layout; eight of them make one
+// 16-deep step with A/B lane l holding k = l / 32 in each.
 //
-// A "k16 fragment" is one lane's 8 operand values for a 16-deep step of the
+// A "k16 fragment" is one lane's 8 operand values of a 16-deep step of the
 // contraction.  Any fixed assignment of contraction indices to (lane half,
 // register) is valid as long as the A and B fragments of one product use the
-// same one; the kernels rely on that freedom to feed softmax results straight
-// from D registers into the next product.
+// same one.  The kernels use that freedom to feed the fp32 D registers of one
+// product (after conversion) straight into the next product as its B operand:
+// register block j of a D tile covers the rows {8j' + 4*(l/32) + 0..3}, which
+// the transposing LDS read below reproduces for the other operand.
+//
+// LDS tiles are stored without padding.  A bf16 row of D elements is D/8
+// granules of 16 bytes; granule g of row r sits at position g ^ sw(r).  The
+// permutation makes both access patterns the kernels use conflict-free on the
+// 64-bank LDS: a 16-lane group reading one granule of 16 consecutive rows
+// (row fragments, ds_read_b128), and a 32-lane group reading four whole
+// granules of four consecutive rows (column fragments, ds_read_b64_tr_b16).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,10 +30,14 @@ namespace fa {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -47,36 +58,122 @@ __device__ __forceinline__ f32x16 mfma_k16(f32x8 a, f32x8 b, f32x16 c) {
   return c;
 }
 
-// ---------------------------------------------------------------- fragments
-// Eight consecutive elements starting at p (16-byte aligned for bf16, 32 for f32).
-__device__ __forceinline__ void frag_rm(bf16x8& f, const bf16* p) { f = *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ void frag_rm(f32x8& f, const float* p) {
-  f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+// ---------------------------------------------------------------- global memory
+// Buffer resource over `bytes` bytes at `base`.  Loads at or beyond `bytes`
+// return zero instead of touching memory, which masks ragged tails for free.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ float load4f(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Eight consecutive elements of row `row`, starting at column c0, of a row-major
+// [*, D] tensor behind `r` (zero past its end) as a k16 fragment.
+template <int D>
+__device__ __forceinline__ void frag_global(bf16x8& f, rsrc_t r, int row, int c0) {
+  f = __builtin_bit_cast(bf16x8, load16(r, (uint32_t)(row * D + c0) * 2u));
+}
+template <int D>
+__device__ __forceinline__ void frag_global(f32x8& f, rsrc_t r, int row, int c0) {
+  const uint32_t o = (uint32_t)(row * D + c0) * 4u;
+  const f32x4 a = __builtin_bit_cast(f32x4, load16(r, o)), b = __builtin_bit_cast(f32x4, load16(r, o + 16));
   f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-__device__ __forceinline__ void frag_zero(bf16x8& f) { f = bf16x8{}; }
-__device__ __forceinline__ void frag_zero(f32x8& f) { f = f32x8{}; }
 
-// Column fragment from a row-major LDS matrix M (row stride `st` elements):
-// the lane owning column c0 + (lane % 32) receives M[rA + 0..3][col] in
-// registers 0..3 and M[rB + 0..3][col] in registers 4..7.  rA and rB may
-// differ between the two lane halves.
-__device__ __forceinline__ void frag_tr(bf16x8& f, const bf16* M, int st, int rA, int rB, int c0) {
-  const int l = lane_id();
-  const int e = (l & 15) >> 2, c = l & 3, g = (l >> 4) & 1;
-  const int col = c0 + g * 16 + 4 * c;
+// ---------------------------------------------------------------- LDS tiles
+template <typename T, int D>
+struct Lay {
+  static constexpr int RB = D * (int)sizeof(T);  // bytes per row
+  static constexpr int G = RB / 16;              // 16-byte granules per row
+  static constexpr int EPG = 16 / (int)sizeof(T);
+  // Position permutation of the granules of row r (float tiles are unpermuted).
+  __device__ static __forceinline__ int sw(int r) {
+    if constexpr (sizeof(T) == 4) {
+      return 0;
+    } else if constexpr (D == 128) {
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+      const int s = r >> 1;  // two 128-byte rows share one 256-byte bank line
+      return ((s & 1) << 2) | ((s >> 1) & 3);
+    }
+  }
+  // Byte offset of element (r, c) in the tile.
+  __device__ static __forceinline__ int off(int r, int c) {
+    return r * RB + (((c / EPG) ^ sw(r)) << 4) + (c % EPG) * (int)sizeof(T);
+  }
+};
+
+// Asynchronous copy of rows [row0, row0 + ROWS) of the row-major [*, D] tensor
+// behind `r` into the LDS tile `dst` (global -> LDS directly, no registers).
+// Rows past the end of the tensor arrive as zeros.  The NW waves of the
+// workgroup split the work; wave `w` issues its share of 1 KB transfers, each
+// lane moving one 16-byte granule to position lane of its kilobyte.
+template <typename T, int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds(rsrc_t r, char* dst, int row0, int w) {
+  typedef Lay<T, D> L;
+  constexpr int CHUNKS = ROWS * L::RB / 1024;
+  static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
+  constexpr int RPC = 64 / L::G;  // rows per kilobyte
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NW; ++i) {
+    const int ch = w * (CHUNKS / NW) + i;
+    const int rr = ch * RPC + lane / L::G;
+    const int g = (lane % L::G) ^ L::sw(rr);
+    const uint32_t voff = (uint32_t)(row0 + rr) * (uint32_t)L::RB + (uint32_t)g * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + ch * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// 64 consecutive floats [row0, row0 + 64) of a vector behind `r` into LDS (one wave).
+__device__ __forceinline__ void vec64_to_lds(rsrc_t r, float* dst, int row0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(row0 + lane_id()) * 4u, 0, 0, 0);
+}
+
+// Waits until this wave's outstanding global -> LDS copies have landed.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Row fragment: elements (r, c0 .. c0+7) of an LDS tile.
+template <int D>
+__device__ __forceinline__ void frag_row(bf16x8& f, const char* s, int r, int c0) {
+  f = *reinterpret_cast<const bf16x8*>(s + Lay<bf16, D>::off(r, c0));
+}
+template <int D>
+__device__ __forceinline__ void frag_row(f32x8& f, const char* s, int r, int c0) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(s + Lay<float, D>::off(r, c0));
+  const f32x4 b = *reinterpret_cast<const f32x4*>(s + Lay<float, D>::off(r, c0 + 4));
+  f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Column fragment: the lane owning column c0 + (lane % 32) receives elements
+// (rA + e, col) in registers e = 0..3 and (rB + e, col) in registers 4 + e.
+// rA and rB may depend on the lane half.  bf16 uses the gfx950 transposing read:
+// within each 16-lane group, result lane j element e is element j % 4 of the 8
+// bytes addressed by lane 4e + j/4.
+template <int D>
+__device__ __forceinline__ void frag_col(bf16x8& f, const char* s, int rA, int rB, int c0) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(M + (rA + e) * st + col));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(M + (rB + e) * st + col));
+  const int l = lane_id();
+  const int e = (l & 15) >> 2, col = c0 + (l & 16) + 4 * (l & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rA + e, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rB + e, col)));
   f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-__device__ __forceinline__ void frag_tr(f32x8& f, const float* M, int st, int rA, int rB, int c0) {
+template <int D>
+__device__ __forceinline__ void frag_col(f32x8& f, const char* s, int rA, int rB, int c0) {
   const int col = c0 + (lane_id() & 31);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { f[e] = M[(rA + e) * st + col]; f[4 + e] = M[(rB + e) * st + col]; }
+  for (int e = 0; e < 4; ++e) {
+    f[e] = *reinterpret_cast<const float*>(s + Lay<float, D>::off(rA + e, col));
+    f[4 + e] = *reinterpret_cast<const float*>(s + Lay<float, D>::off(rB + e, col));
+  }
 }
 
-// Eight fp32 values of a D-register block, taken as a k16 fragment.
+// Eight fp32 values of a D-register block as a k16 fragment.
 __device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (bf16)s[base + j];
@@ -84,6 +181,12 @@ __device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) 
 __device__ __forceinline__ void frag_from(f32x8& f, const f32x16& s, int base) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = s[base + j];
+}
+
+// Zero-fills `bytes` (a multiple of 16) of LDS with NT threads.
+template <int NT>
+__device__ __forceinline__ void lds_zero(char* p, int bytes) {
+  for (int o = threadIdx.x * 16; o < bytes; o += NT * 16) *reinterpret_cast<u32x4*>(p + o) = u32x4{0u, 0u, 0u, 0u};
 }
 
 // ---------------------------------------------------------------- lane exchange
@@ -98,42 +201,42 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------- stores
 // Four consecutive elements at p (8-byte aligned for bf16, 16 for f32).
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
   *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
-// ---------------------------------------------------------------- tile staging
-// A [ROWS x D] tile of a row-major [N x D] matrix staged through registers into
-// LDS (row stride ST elements).  Rows at or beyond n are filled with zeros, so
-// nothing outside the tensor is read.  NT threads cooperate; each moves CH
-// 16-byte chunks.
-template <typename T, int ROWS, int D, int ST, int NT>
-struct TileCopy {
-  static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;                    // chunks per row
-  static constexpr int CH = ROWS * CPR / NT;             // chunks per thread
-  static_assert(ROWS * CPR % NT == 0, "tile must split evenly over the threads");
-  uint4 r[CH];
-  __device__ __forceinline__ void load(const T* g, int row0, int n, int tid) {
+// Stores a transposed accumulator tile: acc[db] holds X^T[d, row] for the
+// 32 rows of this wave (lane = row); writes s * X[row, :] for row < n.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(T* base, int row, int n, const f32x16* acc, float s) {
+  if (row >= n) return;
+  const int hf = lane_id() >> 5;
+  T* p = base + (size_t)row * D;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + c * NT, row = id / CPR, ch = id % CPR;
-      if (row0 + row < n)
-        r[c] = *reinterpret_cast<const uint4*>(g + (size_t)(row0 + row) * D + ch * EPC);
-      else
-        r[c] = uint4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(T* s, int tid) const {
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int id = tid + c * NT, row = id / CPR, ch = id % CPR;
-      *reinterpret_cast<uint4*>(s + row * ST + ch * EPC) = r[c];
-    }
+    for (int g = 0; g < 4; ++g)
+      store4(p + db * 32 + 8 * g + 4 * hf, s * acc[db][4 * g], s * acc[db][4 * g + 1], s * acc[db][4 * g + 2],
+             s * acc[db][4 * g + 3]);
+}
+
+// ---------------------------------------------------------------- work order
+// Maps a linear workgroup index onto (unit, slice) with `units` units per
+// slice-step such that all workgroups of one unit land on the same XCD:
+// workgroups are dealt round-robin over the 8 XCDs, so when `units` is a
+// multiple of 8 the units are split into 8 contiguous ranges, one per XCD.
+// `slot` counts up in dispatch order within an XCD.
+__device__ __forceinline__ void xcd_map(int bid, int units, int& unit, int& slot) {
+  if ((units & 7) == 0) {
+    const int per = units >> 3, x = bid & 7, y = bid >> 3;
+    unit = x * per + y % per;
+    slot = y / per;
+  } else {
+    unit = bid % units;
+    slot = bid / units;
   }
-};
+}
 
 }  // namespace fa

@@ -12,26 +12,35 @@
 // 改进2：并行化策略优化).
 //
 // Mapping onto the CDNA4 compute unit:
-//  * one workgroup = 4 wavefronts = 128 query rows; each wave owns 32 rows;
-//  * K/V tiles of 64 keys are staged through LDS with a double buffer: the
-//    global loads of tile j+1 are in flight while tile j is consumed;
+//  * one workgroup = 4 wavefronts = 128 query rows; each wave owns 32 rows,
+//    whose Q fragments stay in registers for the whole kernel;
+//  * K/V tiles of 64 keys go global -> LDS directly (buffer loads with the LDS
+//    destination), double-buffered: the copies of tile j+1 are in flight while
+//    tile j is consumed; rows past N arrive as zeros;
 //  * scores are produced transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so a
-//    lane owns one query column: the row max / row sum need only one exchange
-//    between the two lane halves (v_permlane32_swap), and the rescale of the
-//    accumulator is a per-lane scalar;
+//    lane owns one query column: the row max / row sum need one exchange
+//    between the two lane halves (v_permlane32_swap) and the rescale is a
+//    per-lane scalar;
 //  * O^T += V^T P^T reuses the probability registers directly as the B
 //    operand; V^T comes from LDS through the gfx950 transposing read;
-//  * softmax runs in the log2 domain: p = exp2(s * scale*log2(e) - m).
+//  * softmax runs in the log2 domain, p = exp2(s * scale*log2(e) - m), and the
+//    running maximum is only moved when a tile raises it by more than 2^8:
+//    any reference point gives the same O = acc / l and lse = m + log2(l), so
+//    skipping small moves saves the accumulator rescale on most tiles while
+//    keeping every p <= 256 (exact in fp32, same relative precision in bf16);
+//  * workgroups of one (batch, head) share an XCD (and its L2), and under the
+//    causal mask the longest query tiles are dispatched first.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
-constexpr int kFwdWaves = 4;
-constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
-constexpr int kFwdBc = 64;              // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;  // query rows per workgroup
+constexpr int kBc = 64;           // keys per tile
+constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
 
 struct FwdArgs {
   const void* q; const void* k; const void* v;
@@ -41,51 +50,44 @@ struct FwdArgs {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   typedef typename Frag<T>::type F;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int KST = D + EPC;      // +16 B per K row
-  constexpr int VST = D + 2 * EPC;  // +32 B per V row
-  constexpr int KS = D / 16;        // contraction steps over d
-  constexpr int DB = D / 32;        // 32-wide blocks of d in the output
-  constexpr int SB = kFwdBc / 32;   // 32-key blocks per tile
-  __shared__ __attribute__((aligned(16))) T sK[2][kFwdBc * KST];
-  __shared__ __attribute__((aligned(16))) T sV[2][kFwdBc * VST];
+  typedef Lay<T, D> L;
+  constexpr int TB = kBc * L::RB;  // bytes of one K or V tile
+  constexpr int KS = D / 16;       // contraction steps over d
+  constexpr int DB = D / 32;       // 32-wide blocks of d in the output
+  __shared__ __attribute__((aligned(1024))) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = a.N;
-
-  // Heaviest (latest) query tiles are dispatched first under the causal mask.
-  const int BH = a.B * a.H;
-  const int bid = blockIdx.x;
-  const int qt = a.nqt - 1 - bid / BH;
-  const int bh = bid % BH;
+  int bh, qi;
+  xcd_map(blockIdx.x, a.B * a.H, bh, qi);
+  const int qt = CAUSAL ? a.nqt - 1 - qi : qi;
   const int b = bh / a.H, h = bh % a.H;
   const int kvh = h / (a.H / a.Hkv);
-  const T* Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * N * D;
-  const T* K = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * N * D;
-  const T* V = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * N * D;
+  const size_t slab = (size_t)N * D;
+  const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
+  const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)bh * slab, slab_bytes);
+  const rsrc_t rK = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
+  const rsrc_t rV = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
 
-  const int q0 = qt * kFwdBr + w * 32;  // first query row of this wave
-  const int myq = q0 + l32;             // query row owned by this lane
-
+  const int q0w = qt * kBr + 32 * w;  // first query row of this wave
+  const int myq = q0w + l32;          // query row owned by this lane
   F qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (myq < N) frag_rm(qf[s], Q + (size_t)myq * D + 16 * s + 8 * hf);
-    else frag_zero(qf[s]);
-  }
+  for (int s = 0; s < KS; ++s) frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
 
-  const int kend = CAUSAL ? min(N, (qt + 1) * kFwdBr) : N;
-  const int nt = (kend + kFwdBc - 1) / kFwdBc;
+  const int kend = CAUSAL ? min(N, (qt + 1) * kBr) : N;
+  const int nt = (kend + kBc - 1) / kBc;
 
-  TileCopy<T, kFwdBc, D, KST, kFwdThreads> kc;
-  TileCopy<T, kFwdBc, D, VST, kFwdThreads> vc;
-  kc.load(K, 0, N, tid);
-  vc.load(V, 0, N, tid);
-  kc.store(sK[0], tid);
-  vc.store(sV[0], tid);
+  // Zero the tiles once so that nothing read from LDS is ever uninitialised.
+  lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
+  lds_zero<kThreads>(sV0, TB); lds_zero<kThreads>(sV1, TB);
+  __syncthreads();
+  tile_to_lds<T, D, kBc, kWaves>(rK, sK0, 0, w);
+  tile_to_lds<T, D, kBc, kWaves>(rV, sV0, 0, w);
+  wait_copies();
   __syncthreads();
 
   float m = -INFINITY, lsum = 0.f;
@@ -93,107 +95,108 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  for (int j = 0; j < nt; ++j) {
-    const int cur = j & 1;
-    const int k0 = j * kFwdBc;
-    if (j + 1 < nt) {
-      kc.load(K, k0 + kFwdBc, N, tid);
-      vc.load(V, k0 + kFwdBc, N, tid);
+  auto tile = [&](const char* sK, const char* sV, int k0) {
+    if (CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
+    // S^T = K Q^T for this wave's 32 queries.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        F kf;
+        frag_row<D>(kf, sK, kb * 32 + l32, 16 * ks + 8 * hf);
+        s[kb] = mfma_k16(kf, qf[ks], s[kb]);
+      }
     }
-    if (!CAUSAL || k0 <= q0 + 31) {
-      const T* Kt = sK[cur];
-      const T* Vt = sV[cur];
-      // S^T = K Q^T for this wave's 32 queries.
-      f32x16 s[SB];
+    // Causal mask on diagonal tiles; keys past N on the last tile.
+    if (CAUSAL ? (k0 + kBc - 1 > q0w) : (k0 + kBc > N)) {
 #pragma unroll
-      for (int kb = 0; kb < SB; ++kb) {
-        s[kb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          F kf;
-          frag_rm(kf, Kt + (kb * 32 + l32) * KST + 16 * ks + 8 * hf);
-          s[kb] = mfma_k16(kf, qf[ks], s[kb]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (CAUSAL ? key > myq : key >= N) s[kb][i] = -INFINITY;
         }
-      }
-      // Mask keys beyond N and, under the causal mask, keys after the query.
-      if (k0 + kFwdBc > N || (CAUSAL && k0 + kFwdBc - 1 > q0)) {
+    }
+    float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (key >= N || (CAUSAL && key > myq)) s[kb][i] = -INFINITY;
-          }
-      }
-      // Online softmax update (log2 domain).
-      float mt = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < SB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-      mt = fmaxf(mt, other_half(mt));
-      const float mnew = fmaxf(m, mt * a.c);
-      const float alpha = fast_exp2(m - mnew);
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
+    mt = fmaxf(mt, other_half(mt)) * a.c;
+    if (__ballot(mt > m + kSlack)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
       m = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-      float ps = 0.f;
+    }
+    float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < SB; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
-          s[kb][i] = p;
-          ps += p;
-        }
-      lsum += ps;
-      // O^T += V^T P^T, 16 keys per step.
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
+        s[kb][i] = p;
+        ps += p;
+      }
+    lsum += ps;
+    // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
-      for (int t = 0; t < kFwdBc / 16; ++t) {
-        F pf;
-        frag_from(pf, s[t >> 1], (t & 1) * 8);
-        const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
+    for (int t = 0; t < kBc / 16; ++t) {
+      F pf;
+      frag_from(pf, s[t >> 1], (t & 1) * 8);
+      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          F vf;
-          frag_tr(vf, Vt, VST, rA, rA + 8, db * 32);
-          acc[db] = mfma_k16(vf, pf, acc[db]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        F vf;
+        frag_col<D>(vf, sV, rA, rA + 8, db * 32);
+        acc[db] = mfma_k16(vf, pf, acc[db]);
       }
     }
+  };
+
+  // Two tiles per iteration so that each buffer is a distinct LDS object.
+  for (int j = 0; j < nt; j += 2) {
     if (j + 1 < nt) {
-      kc.store(sK[cur ^ 1], tid);
-      vc.store(sV[cur ^ 1], tid);
+      tile_to_lds<T, D, kBc, kWaves>(rK, sK1, (j + 1) * kBc, w);
+      tile_to_lds<T, D, kBc, kWaves>(rV, sV1, (j + 1) * kBc, w);
     }
+    tile(sK0, sV0, j * kBc);
+    wait_copies();
+    __syncthreads();
+    if (j + 1 >= nt) break;
+    if (j + 2 < nt) {
+      tile_to_lds<T, D, kBc, kWaves>(rK, sK0, (j + 2) * kBc, w);
+      tile_to_lds<T, D, kBc, kWaves>(rV, sV0, (j + 2) * kBc, w);
+    }
+    tile(sK1, sV1, (j + 1) * kBc);
+    wait_copies();
     __syncthreads();
   }
 
   lsum += other_half(lsum);
-  if (myq < N) {
-    const float inv = 1.f / lsum;
-    T* O = reinterpret_cast<T*>(a.o) + (size_t)bh * N * D + (size_t)myq * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hf;
-        store4(O + d, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-      }
-    if (hf == 0) a.lse[(size_t)bh * N + myq] = (m + __log2f(lsum)) * kLn2;
-  }
+  store_rows<T, D>(reinterpret_cast<T*>(a.o) + (size_t)bh * slab, myq, N, acc, 1.f / lsum);
+  if (hf == 0 && myq < N) a.lse[(size_t)bh * N + myq] = (m + __log2f(lsum)) * kLn2;
 }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel_bf16(FwdArgs a) { fwd_body<bf16, D, CAUSAL>(a); }
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel_f32(FwdArgs a) { fwd_body<float, D, CAUSAL>(a); }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N;
-  a.nqt = (p.N + kFwdBr - 1) / kFwdBr;
+  a.nqt = (p.N + kBr - 1) / kBr;
   a.c = p.scale * kLog2e;
-  const long grid = (long)a.nqt * p.B * p.H;
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kFwdThreads), 0, stream, a);
+  const dim3 grid((unsigned)((long)a.nqt * p.B * p.H));
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

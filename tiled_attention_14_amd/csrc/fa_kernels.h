@@ -8,6 +8,10 @@ namespace fa {
 
 enum Dtype { kBF16 = 0, kF32 = 1 };
 
+// Key rows per workgroup of the dK/dV kernel and query rows per step of its loop.
+constexpr int kDkdvKeys = 128;
+constexpr int kDkdvQRows = 64;
+
 struct FwdParams {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
@@ -21,8 +25,10 @@ struct BwdParams {
   const void* q; const void* k; const void* v;
   const void* o; const void* dO; const float* lse;
   void* dq; void* dk; void* dv;
-  float* delta;    // [B, H, N] workspace: D_i = sum_c dO_ic O_ic
-  float* dq_acc;   // [B, H, N, d] fp32 accumulator (bf16) or dq itself (f32)
+  float* delta;   // [B, H, N] workspace: D_i = sum_c dO_ic O_ic
+  float* lse2;    // [B, H, N] workspace: lse_i * log2(e)
+  float* part;    // [nsplit, 2, B, Hkv, N, d] float32 partial dK / dV (nsplit > 1 only)
+  int nsplit;     // query-head slices of a GQA group handled by separate workgroups
   int B, H, Hkv, N, d;
   float scale;
   bool causal;
@@ -30,10 +36,11 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
-// The three backward phases, in stream order: D and dQ-accumulator zeroing,
-// the main kernel, and (bf16 only) the dQ conversion.
+// Backward phases, in stream order: preprocess (D and lse2), then the dK/dV
+// kernel (plus the reduction of its partials when nsplit > 1) and the dQ
+// kernel, which are independent of each other.
 hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -1,7 +1,7 @@
 """Thin Python binding of the C ABI in ``include/fa.h``.
 
-``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_main``,
-``fa_bwd_finalize``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
+``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``,
+``fa_bwd_dq``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
 the C names and argument order; pointer arguments accept an integer device
 address or any object with ``data_ptr()`` (a torch tensor), and ``stream`` an
 integer ``hipStream_t``, a torch stream, or ``None`` for torch's current stream.
@@ -44,10 +44,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = I
         L.fa_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, I, P, S, P]
         L.fa_bwd_preprocess.restype = I
-        L.fa_bwd_main.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
-        L.fa_bwd_main.restype = I
-        L.fa_bwd_finalize.argtypes = [P, I, I, I, I, I, I, P, S, P]
-        L.fa_bwd_finalize.restype = I
+        L.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        L.fa_bwd_dkdv.restype = I
+        L.fa_bwd_dq.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        L.fa_bwd_dq.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -89,21 +89,23 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtyp
                         _stream(stream))
 
 
-def fa_bwd_preprocess(o, dO, dq, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
-    return lib().fa_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(dq), B, H, Hkv, N, d, int(dtype),
+def fa_bwd_preprocess(o, dO, lse, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_preprocess(_ptr(o), _ptr(dO), _ptr(lse), B, H, Hkv, N, d, int(dtype),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
-def fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype,
+def fa_bwd_dkdv(q, k, v, dO, dk, dv, B, H, Hkv, N, d, scale, causal, dtype,
                 workspace, workspace_bytes, stream=None) -> int:
-    return lib().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+    return lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dk), _ptr(dv),
                              B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
-def fa_bwd_finalize(dq, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
-    return lib().fa_bwd_finalize(_ptr(dq), B, H, Hkv, N, d, int(dtype), _ptr(workspace),
-                                 int(workspace_bytes), _stream(stream))
+def fa_bwd_dq(q, k, v, dO, dq, B, H, Hkv, N, d, scale, causal, dtype,
+              workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq),
+                           B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
+                           _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def fa_status_string(status: int) -> str:
