@@ -99,6 +99,49 @@ def test_workload_llama2_70b_gqa_causal():
     _sampled(synth.WORKLOADS["llama2_70b_gqa_causal_n8192_d128"])
 
 
+def _identities(w, inp, g, tol=0.02):
+    """Exact identities of the backward pass (they hold for any inputs; see the
+    oracle's pins) checked in float64 on the full GPU tensors.  Each residual is
+    compared with the root-sum-square of the terms it adds up, which bounds the
+    rounding of the bf16 outputs (unit roundoff 2^-9) by a wide margin."""
+    q, k, v, do = inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do")
+    o, dq, dk, dv = (host64(g[n]) for n in ("o", "dq", "dk", "dv"))
+    for name, x in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.all(np.isfinite(x)), f"{name} has non-finite values"
+    B, Hkv, gsz = w.B, w.Hkv, w.H // w.Hkv
+    grp = lambda x: x.reshape(B, Hkv, gsz, *x.shape[2:])
+    res = {
+        # sum_j dV_j = sum_i dO_i over the group
+        "sum dV = sum dO": (dv.sum(2) - grp(do).sum((2, 3)), np.sqrt((dv ** 2).sum(2) + (grp(do) ** 2).sum((2, 3)))),
+        # sum_j dK_j = 0
+        "sum dK = 0": (dk.sum(2), np.sqrt((dk ** 2).sum(2))),
+        # sum_i Q_i.dQ_i = sum_j K_j.dK_j
+        "Q.dQ = K.dK": (grp(q * dq).sum((2, 3, 4)) - (k * dk).sum((2, 3)),
+                        np.sqrt((grp(q * dq) ** 2).sum((2, 3, 4)) + ((k * dk) ** 2).sum((2, 3)))),
+        # sum_j V_j.dV_j = sum_i dO_i.O_i
+        "V.dV = dO.O": ((v * dv).sum((2, 3)) - grp(do * o).sum((2, 3, 4)),
+                        np.sqrt(((v * dv) ** 2).sum((2, 3)) + (grp(do * o) ** 2).sum((2, 3, 4)))),
+    }
+    worst = {n: float(np.max(np.abs(r) / s)) for n, (r, s) in res.items()}
+    say(f"[identities] {w.name}: " + ", ".join(f"{n}: {x:.2e}" for n, x in worst.items()))
+    bad = {n: x for n, x in worst.items() if not x <= tol}
+    assert not bad, f"identity residuals above {tol}: {bad}"
+
+
+def test_workload_long_seq_causal():
+    """N = 65536 with Q, K ~ N(0, 4): sampled rows against the oracle, the exact
+    identities and a NaN/Inf scan on the full tensors."""
+    w = synth.WORKLOADS["long_seq_causal_n65536_d128"]
+    inp, full = _sampled(w)
+    _identities(w, inp, full)
+
+
+def test_identities_llama2_7b_causal():
+    w = synth.WORKLOADS["llama2_7b_causal_n4096_d128"]
+    inp = synth.make_inputs(w)
+    _identities(w, inp, run_gpu(w, to_device(inp)))
+
+
 @pytest.mark.parametrize("dt,d,causal,heads", [("bf16", 128, True, (4, 2)), ("bf16", 64, False, (4, 4)),
                                                ("f32", 64, True, (4, 1))])
 def test_phases_equal_fa_bwd(dt, d, causal, heads):

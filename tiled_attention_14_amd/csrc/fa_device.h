@@ -29,7 +29,9 @@
 namespace fa {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -51,6 +53,9 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // ---------------------------------------------------------------- products
 __device__ __forceinline__ f32x16 mfma_k16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_k16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma_k16(f32x8 a, f32x8 b, f32x16 c) {
 #pragma unroll
@@ -154,14 +159,22 @@ __device__ __forceinline__ void frag_row(f32x8& f, const char* s, int r, int c0)
 // rA and rB may depend on the lane half.  bf16 uses the gfx950 transposing read:
 // within each 16-lane group, result lane j element e is element j % 4 of the 8
 // bytes addressed by lane 4e + j/4.
-template <int D>
-__device__ __forceinline__ void frag_col(bf16x8& f, const char* s, int rA, int rB, int c0) {
+template <int D, typename V8>
+__device__ __forceinline__ void frag_col16(V8& f, const char* s, int rA, int rB, int c0) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const int l = lane_id();
   const int e = (l & 15) >> 2, col = c0 + (l & 16) + 4 * (l & 3);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rA + e, col)));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rB + e, col)));
-  f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  f = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <int D>
+__device__ __forceinline__ void frag_col(bf16x8& f, const char* s, int rA, int rB, int c0) {
+  frag_col16<D>(f, s, rA, rB, c0);
+}
+template <int D>
+__device__ __forceinline__ void frag_col(f16x8& f, const char* s, int rA, int rB, int c0) {
+  frag_col16<D>(f, s, rA, rB, c0);
 }
 template <int D>
 __device__ __forceinline__ void frag_col(f32x8& f, const char* s, int rA, int rB, int c0) {
@@ -178,9 +191,28 @@ __device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) 
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = (bf16)s[base + j];
 }
+__device__ __forceinline__ void frag_from(f16x8& f, const f32x16& s, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (f16)s[base + j];
+}
 __device__ __forceinline__ void frag_from(f32x8& f, const f32x16& s, int base) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = s[base + j];
+}
+
+// bf16 -> fp16 conversion of the 1 KB LDS chunks [c0, c0 + n) of `src` into
+// the same positions of `dst` (one 16-byte granule per lane and chunk).  Exact
+// for |x| in [2^-14, 65504]; smaller magnitudes keep an absolute error below
+// 2^-25.
+__device__ __forceinline__ void lds_bf16_to_f16(const char* src, char* dst, int c0, int n) {
+  const int lane = lane_id();
+  for (int c = c0; c < c0 + n; ++c) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + c * 1024 + lane * 16);
+    f16x8 y;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = (f16)(float)x[j];
+    *reinterpret_cast<f16x8*>(dst + c * 1024 + lane * 16) = y;
+  }
 }
 
 // Zero-fills `bytes` (a multiple of 16) of LDS with NT threads.

@@ -22,12 +22,19 @@
 //    between the two lane halves (v_permlane32_swap) and the rescale is a
 //    per-lane scalar;
 //  * O^T += V^T P^T reuses the probability registers directly as the B
-//    operand; V^T comes from LDS through the gfx950 transposing read;
+//    operand; V^T comes from LDS through the gfx950 transposing read.  For
+//    bf16 inputs this product runs in fp16 (P and V converted, fp32
+//    accumulation): fp16 keeps 3 more significand bits than bf16, which bounds
+//    the error of O before its final bf16 rounding by about 2^-12 |O| instead
+//    of 2^-9 |O|, so that peaked rows of long sequences stay within 1e-2 after
+//    that rounding.  Each wave converts the part of the V tile it copied
+//    itself (bf16 staging buffer -> fp16 tile), so the conversion needs no
+//    extra barrier;
 //  * softmax runs in the log2 domain, p = exp2(s * scale*log2(e) - m), and the
 //    running maximum is only moved when a tile raises it by more than 2^8:
 //    any reference point gives the same O = acc / l and lse = m + log2(l), so
 //    skipping small moves saves the accumulator rescale on most tiles while
-//    keeping every p <= 256 (exact in fp32, same relative precision in bf16);
+//    keeping every p <= 256 (far inside the fp16 range);
 //  * workgroups of one (batch, head) share an XCD (and its L2), and under the
 //    causal mask the longest query tiles are dispatched first.
 #include "fa_device.h"
@@ -49,14 +56,23 @@ struct FwdArgs {
   float c;  // scale * log2(e)
 };
 
+// Operand type of the P V product: fp16 for bf16 inputs, fp32 for fp32 inputs.
+template <typename T> struct PvFrag;
+template <> struct PvFrag<bf16> { typedef f16x8 type; };
+template <> struct PvFrag<float> { typedef f32x8 type; };
+
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   typedef typename Frag<T>::type F;
+  typedef typename PvFrag<T>::type PF;
   typedef Lay<T, D> L;
-  constexpr int TB = kBc * L::RB;  // bytes of one K or V tile
-  constexpr int KS = D / 16;       // contraction steps over d
-  constexpr int DB = D / 32;       // 32-wide blocks of d in the output
+  constexpr bool kConv = sizeof(T) == 2;  // V staged as bf16, consumed as fp16
+  constexpr int TB = kBc * L::RB;         // bytes of one K or V tile
+  constexpr int KS = D / 16;              // contraction steps over d
+  constexpr int DB = D / 32;              // 32-wide blocks of d in the output
+  constexpr int CPW = TB / 1024 / kWaves; // 1 KB copy chunks per wave and tile
   __shared__ __attribute__((aligned(1024))) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
+  __shared__ __attribute__((aligned(1024))) char sVr[kConv ? TB : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -84,10 +100,20 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   // Zero the tiles once so that nothing read from LDS is ever uninitialised.
   lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
   lds_zero<kThreads>(sV0, TB); lds_zero<kThreads>(sV1, TB);
+  if constexpr (kConv) lds_zero<kThreads>(sVr, TB);
   __syncthreads();
-  tile_to_lds<T, D, kBc, kWaves>(rK, sK0, 0, w);
-  tile_to_lds<T, D, kBc, kWaves>(rV, sV0, 0, w);
+  // V tile j+1 is copied into the staging buffer (bf16) or straight into its
+  // tile (fp32); the staging buffer is converted into the tile by the same wave.
+  auto copy_kv = [&](char* sK, char* sV, int k0) {
+    tile_to_lds<T, D, kBc, kWaves>(rK, sK, k0, w);
+    tile_to_lds<T, D, kBc, kWaves>(rV, kConv ? sVr : sV, k0, w);
+  };
+  auto finish_v = [&](char* sV) {
+    if constexpr (kConv) lds_bf16_to_f16(sVr, sV, w * CPW, CPW);
+  };
+  copy_kv(sK0, sV0, 0);
   wait_copies();
+  finish_v(sV0);
   __syncthreads();
 
   float m = -INFINITY, lsum = 0.f;
@@ -144,12 +170,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
     for (int t = 0; t < kBc / 16; ++t) {
-      F pf;
+      PF pf;
       frag_from(pf, s[t >> 1], (t & 1) * 8);
       const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        F vf;
+        PF vf;
         frag_col<D>(vf, sV, rA, rA + 8, db * 32);
         acc[db] = mfma_k16(vf, pf, acc[db]);
       }
@@ -158,20 +184,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   // Two tiles per iteration so that each buffer is a distinct LDS object.
   for (int j = 0; j < nt; j += 2) {
-    if (j + 1 < nt) {
-      tile_to_lds<T, D, kBc, kWaves>(rK, sK1, (j + 1) * kBc, w);
-      tile_to_lds<T, D, kBc, kWaves>(rV, sV1, (j + 1) * kBc, w);
-    }
+    if (j + 1 < nt) copy_kv(sK1, sV1, (j + 1) * kBc);
     tile(sK0, sV0, j * kBc);
     wait_copies();
+    if (j + 1 < nt) finish_v(sV1);
     __syncthreads();
     if (j + 1 >= nt) break;
-    if (j + 2 < nt) {
-      tile_to_lds<T, D, kBc, kWaves>(rK, sK0, (j + 2) * kBc, w);
-      tile_to_lds<T, D, kBc, kWaves>(rV, sV0, (j + 2) * kBc, w);
-    }
+    if (j + 2 < nt) copy_kv(sK0, sV0, (j + 2) * kBc);
     tile(sK1, sV1, (j + 1) * kBc);
     wait_copies();
+    if (j + 2 < nt) finish_v(sV0);
     __syncthreads();
   }
 
