@@ -1,6 +1,6 @@
 // fa_api.cpp — the C ABI of include/fa.h: argument validation, workspace
 // layout and kernel dispatch.  Nothing here allocates, prints or throws.
-#include "../../include/fa.h"
+#include "fa.h"
 
 #include <algorithm>
 #include <cmath>

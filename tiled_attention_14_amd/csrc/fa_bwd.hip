@@ -35,6 +35,8 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -146,6 +148,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const int nq = nqt - qstart;
   const int total = gs * nq;
 
+  RowFrags<T, D> rf;
+  ColFrags<T, D> cf;
+  TileCopy<T, D, kQRows, kWaves> tc;
+  rf.init();
+  cf.init();
+  tc.init(w);
+
   lds_zero<kThreads>(sQ0, TB); lds_zero<kThreads>(sQ1, TB);
   lds_zero<kThreads>(sO0, TB); lds_zero<kThreads>(sO1, TB);
   lds_zero<kThreads>(reinterpret_cast<char*>(sL0), 4 * kQRows);
@@ -159,34 +168,44 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const int hq = h0 + it / nq;
     const int qb0 = (qstart + it % nq) * kQRows;
     const size_t head = (size_t)b * a.H + hq;
-    const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + head * slab, slab_bytes);
-    const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.dO) + head * slab, slab_bytes);
-    tile_to_lds<T, D, kQRows, kWaves>(rQ, bq, qb0, w);
-    tile_to_lds<T, D, kQRows, kWaves>(rO, bo, qb0, w);
+    tc.issue(reinterpret_cast<const T*>(a.q) + head * slab, N, qb0, bq);
+    tc.issue(reinterpret_cast<const T*>(a.dO) + head * slab, N, qb0, bo);
     if (w == 0) vec64_to_lds(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
     if (w == 1) vec64_to_lds(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
   };
+  // Steps that touch the causal diagonal or the ragged end of the sequence.
+  auto masked = [&](int it) {
+    const int qi = it % nq;
+    return (CAUSAL && qi < kKeys / kQRows) || (qstart + qi + 1) * kQRows > N;
+  };
 
-  auto step = [&](const char* sQ, const char* sO, const float* sL, const float* sD, int it) {
+  // One step: S = Q K^T, dP = dO V^T, P and dS, then dV^T += dO^T P and
+  // dK^T += Q^T dS, in two 32-row halves (mb) so that the vector work of one
+  // half runs between the matrix products of the other:
+  //   products S/dP(0), S/dP(1) | softmax(0) ; products dV/dK(0) | softmax(1) ;
+  //   products dV/dK(1).
+  // MASK selects the general form; other steps take the mask-free form.
+  auto step = [&](const char* sQ, const char* sO, const float* sL, const float* sD, int it, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int qb0 = (qstart + it % nq) * kQRows;
-    if (CAUSAL && qb0 + kQRows - 1 < kw) return;  // every query of the step is before every key of the wave
+    if (MASK && CAUSAL && qb0 + kQRows - 1 < kw) return;  // every query of the step is before every key of the wave
     f32x16 s[MB], dp[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    auto sdp = [&](int mb) {
       s[mb] = f32x16{};
       dp[mb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         F qa, oa;
-        frag_row<D>(qa, sQ, mb * 32 + l32, 16 * ks + 8 * hf);
-        frag_row<D>(oa, sO, mb * 32 + l32, 16 * ks + 8 * hf);
+        rf.read(qa, sQ, mb, ks);
+        rf.read(oa, sO, mb, ks);
         s[mb] = mfma_k16(qa, kf[ks], s[mb]);
         dp[mb] = mfma_k16(oa, vf[ks], dp[mb]);
       }
-    }
-    const bool need_mask = (CAUSAL && kw + 31 > qb0) || (qb0 + kQRows > N);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    };
+    // Masked when key > q (causal) or q >= N: q - key = ql - lim.
+    const int lim = mykey - qb0 - 4 * hf;
+    const int qlim = N - 1 - qb0 - 4 * hf;
+    auto softmax = [&](int mb) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int ql0 = mb * 32 + 8 * g4 + 4 * hf;
@@ -196,30 +215,122 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
           float p = fast_exp2(__builtin_fmaf(s[mb][i], a.c, -lv[e]));
-          if (need_mask) {
-            const int q = qb0 + ql0 + e;
-            if ((CAUSAL && mykey > q) || q >= N) p = 0.f;
+          if (MASK) {
+            const int c = mb * 32 + 8 * g4 + e;  // ql - 4 hf
+            if ((CAUSAL && c < lim) || c > qlim) p = 0.f;
           }
           s[mb][i] = p;
           dp[mb][i] = p * (dp[mb][i] - dd[e]);
         }
       }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 query rows per step.
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for the 32 query rows of half mb.
+    auto dvdk = [&](int mb) {
 #pragma unroll
-    for (int t = 0; t < 2 * MB; ++t) {
-      F pf, dsf;
-      frag_from(pf, s[t >> 1], (t & 1) * 8);
-      frag_from(dsf, dp[t >> 1], (t & 1) * 8);
-      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
+      for (int t = 2 * mb; t < 2 * mb + 2; ++t) {
+        F pf, dsf;
+        frag_from(pf, s[t >> 1], (t & 1) * 8);
+        frag_from(dsf, dp[t >> 1], (t & 1) * 8);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        F oa, qa;
-        frag_col<D>(oa, sO, rA, rA + 8, db * 32);
-        dv[db] = mfma_k16(oa, pf, dv[db]);
-        frag_col<D>(qa, sQ, rA, rA + 8, db * 32);
-        dk[db] = mfma_k16(qa, dsf, dk[db]);
+        for (int db = 0; db < DB; ++db) {
+          F oa, qa;
+          cf.read(oa, sO, t, db);
+          dv[db] = mfma_k16(oa, pf, dv[db]);
+          cf.read(qa, sQ, t, db);
+          dk[db] = mfma_k16(qa, dsf, dk[db]);
+        }
       }
+    };
+    static_assert(MB == 2, "two query halves per step");
+    sdp(0);
+    sdp(1);
+    softmax(0);
+    dvdk(0);
+    softmax(1);
+    dvdk(1);
+  };
+
+  // The mask-free step, software-pipelined by hand: LDS reads are issued two
+  // slots ahead of their products, and each slot pairs two matrix products
+  // with a share of the softmax of the half whose scores are already done.
+  // sched_barrier(0) closes every slot, so the compiler keeps this order.
+  //   phase 1: S/dP of both halves; softmax(0) in the last slots
+  //   phase 2: dV/dK of half 0; softmax(1)
+  //   phase 3: dV/dK of half 1
+  auto step_full = [&](const char* sQ, const char* sO, const float* sL, const float* sD) {
+    constexpr int NX = MB * KS;      // slots of phase 1
+    constexpr int NY = 2 * MB * DB;  // slots of phases 2 and 3
+    constexpr int AH = 2;            // read-ahead in slots
+    f32x16 s[MB], dp[MB];
+    F qa[NX], oa[NX], oT[NY], qT[NY];
+    f32x4 lv[MB][4], dd[MB][4];
+    auto rd = [&](int x) {
+      rf.read(qa[x], sQ, x / KS, x % KS);
+      rf.read(oa[x], sO, x / KS, x % KS);
+    };
+    auto rdT = [&](int y) {
+      cf.read(oT[y], sO, y / DB, y % DB);
+      cf.read(qT[y], sQ, y / DB, y % DB);
+    };
+    auto sm = [&](int mb, int i) {
+      const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.c, -lv[mb][i >> 2][i & 3]));
+      s[mb][i] = p;
+      dp[mb][i] = p * (dp[mb][i] - dd[mb][i >> 2][i & 3]);
+    };
+    F pf[2 * MB], dsf[2 * MB];
+    auto cvt = [&](int t) {
+      frag_from(pf[t], s[t >> 1], (t & 1) * 8);
+      frag_from(dsf[t], dp[t >> 1], (t & 1) * 8);
+    };
+#pragma unroll
+    for (int x = 0; x < AH; ++x) rd(x);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        lv[mb][g4] = *reinterpret_cast<const f32x4*>(sL + mb * 32 + 8 * g4 + 4 * hf);
+        dd[mb][g4] = *reinterpret_cast<const f32x4*>(sD + mb * 32 + 8 * g4 + 4 * hf);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 1
+    constexpr int S0 = KS + 2;  // first slot with softmax(0) work
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      if (x + AH < NX) rd(x + AH);
+      const int mb = x / KS, ks = x % KS;
+      s[mb] = mfma_k16(qa[x], kf[ks], ks == 0 ? f32x16{} : s[mb]);
+      dp[mb] = mfma_k16(oa[x], vf[ks], ks == 0 ? f32x16{} : dp[mb]);
+      if (x >= S0) {
+#pragma unroll
+        for (int i = (x - S0) * 16 / (NX - S0); i < (x - S0 + 1) * 16 / (NX - S0); ++i) sm(0, i);
+      }
+      if (x == NX - 1) { cvt(0); cvt(1); }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // phases 2 and 3
+#pragma unroll
+    for (int y = 0; y < AH; ++y) rdT(y);
+    constexpr int NY2 = NY / 2;  // slots of phase 2
+#pragma unroll
+    for (int y = 0; y < NY; ++y) {
+      if (y + AH < NY) rdT(y + AH);
+      const int t = y / DB, db = y % DB;
+      dv[db] = mfma_k16(oT[y], pf[t], dv[db]);
+      dk[db] = mfma_k16(qT[y], dsf[t], dk[db]);
+      if (y >= 1 && y < NY2) {
+#pragma unroll
+        for (int i = (y - 1) * 16 / (NY2 - 1); i < y * 16 / (NY2 - 1); ++i) sm(1, i);
+      }
+      if (y == NY2 - 1) { cvt(2); cvt(3); }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  typedef std::integral_constant<bool, false> Full;
+  typedef std::integral_constant<bool, true> Any;
+  auto run = [&](const char* sQ, const char* sO, const float* sL, const float* sD, int it) {
+    if (masked(it)) step(sQ, sO, sL, sD, it, Any());
+    else step_full(sQ, sO, sL, sD);
   };
 
   if (total > 0) fetch(0, sQ0, sO0, sL0, sD0);
@@ -227,12 +338,12 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   __syncthreads();
   for (int it = 0; it < total; it += 2) {
     if (it + 1 < total) fetch(it + 1, sQ1, sO1, sL1, sD1);
-    step(sQ0, sO0, sL0, sD0, it);
+    run(sQ0, sO0, sL0, sD0, it);
     wait_copies();
     __syncthreads();
     if (it + 1 >= total) break;
     if (it + 2 < total) fetch(it + 2, sQ0, sO0, sL0, sD0);
-    step(sQ1, sO1, sL1, sD1, it + 1);
+    run(sQ1, sO1, sL1, sD1, it + 1);
     wait_copies();
     __syncthreads();
   }
@@ -288,9 +399,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   const int kvh = h / (a.H / a.Hkv);
   const size_t slab = (size_t)N * D;
   const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
-  const rsrc_t rK = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
-  const rsrc_t rV = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
-
   const int q0w = qt * kQTile + 32 * w;
   const int myq = q0w + l32;
   F qf[KS], of[KS];
@@ -309,12 +417,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kQTile) : N;
   const int nt = (kend + kKTile - 1) / kKTile;
+  const T* Kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab;
+  const T* Vh = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab;
+  RowFrags<T, D> rf;
+  ColFrags<T, D> cf;
+  TileCopy<T, D, kKTile, kWaves> tc;
+  rf.init();
+  cf.init();
+  tc.init(w);
 
   lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
   lds_zero<kThreads>(sV0, TB); lds_zero<kThreads>(sV1, TB);
   __syncthreads();
-  tile_to_lds<T, D, kKTile, kWaves>(rK, sK0, 0, w);
-  tile_to_lds<T, D, kKTile, kWaves>(rV, sV0, 0, w);
+  auto copy_kv = [&](char* sK, char* sV, int k0) {
+    tc.issue(Kh, N, k0, sK);
+    tc.issue(Vh, N, k0, sV);
+  };
+  copy_kv(sK0, sV0, 0);
   wait_copies();
   __syncthreads();
 
@@ -322,66 +441,69 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  auto tile = [&](const char* sK, const char* sV, int k0) {
-    if (CAUSAL && k0 > q0w + 31) return;
-    // S^T = K Q^T and dP^T = V dO^T for this wave's 32 queries.
-    f32x16 s[2], dp[2];
+  // One K/V tile: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.  MASK
+  // selects the general form (causal diagonal, keys past N, waves with
+  // nothing to do); tiles full for the whole workgroup take the mask-free form.
+  auto tile = [&](const char* sK, const char* sV, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (MASK && CAUSAL && k0 > q0w + 31) return;
+    // key > myq (causal) or key >= N: with lim = myq - k0 - 4 hf (resp. N - 1 - k0 - 4 hf)
+    // the test is a compare of lim with a per-register constant.
+    const int lim = (CAUSAL ? myq : N - 1) - k0 - 4 * hf;
+    // Two 32-key halves, so that only one half's S and dP are live at a time.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         F kf, vf;
-        frag_row<D>(kf, sK, kb * 32 + l32, 16 * ks + 8 * hf);
-        frag_row<D>(vf, sV, kb * 32 + l32, 16 * ks + 8 * hf);
-        s[kb] = mfma_k16(kf, qf[ks], s[kb]);
-        dp[kb] = mfma_k16(vf, of[ks], dp[kb]);
+        rf.read(kf, sK, kb, ks);
+        rf.read(vf, sV, kb, ks);
+        s = mfma_k16(kf, qf[ks], s);
+        dp = mfma_k16(vf, of[ks], dp);
       }
-    }
-    const bool need_mask = CAUSAL ? (k0 + kKTile - 1 > q0w) : (k0 + kKTile > N);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -l2));
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (CAUSAL ? key > myq : key >= N) p = 0.f;
+        float p = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
+        if (MASK && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
+        dp[i] = p * (dp[i] - dd);
+      }
+      // dQ^T += K^T dS^T, 16 keys per step.
+#pragma unroll
+      for (int t = 2 * kb; t < 2 * kb + 2; ++t) {
+        F dsf;
+        frag_from(dsf, dp, (t & 1) * 8);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          F kf;
+          cf.read(kf, sK, t, db);
+          acc[db] = mfma_k16(kf, dsf, acc[db]);
         }
-        dp[kb][i] = p * (dp[kb][i] - dd);
       }
-    // dQ^T += K^T dS^T, 16 keys per step.
-#pragma unroll
-    for (int t = 0; t < kKTile / 16; ++t) {
-      F dsf;
-      frag_from(dsf, dp[t >> 1], (t & 1) * 8);
-      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        F kf;
-        frag_col<D>(kf, sK, rA, rA + 8, db * 32);
-        acc[db] = mfma_k16(kf, dsf, acc[db]);
-      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart: bounds register pressure
     }
   };
+  typedef std::integral_constant<bool, false> Full;
+  typedef std::integral_constant<bool, true> Any;
 
-  for (int j = 0; j < nt; j += 2) {
-    if (j + 1 < nt) {
-      tile_to_lds<T, D, kKTile, kWaves>(rK, sK1, (j + 1) * kKTile, w);
-      tile_to_lds<T, D, kKTile, kWaves>(rV, sV1, (j + 1) * kKTile, w);
-    }
-    tile(sK0, sV0, j * kKTile);
+  // Tiles [0, jfull) are unmasked for every query of the workgroup.
+  const int jfull = min(nt, CAUSAL ? (qt * kQTile) / kKTile : N / kKTile);
+  auto step = [&](int j, char* sKc, char* sVc, char* sKn, char* sVn, auto mask_tag) {
+    if (j + 1 < nt) copy_kv(sKn, sVn, (j + 1) * kKTile);
+    tile(sKc, sVc, j * kKTile, mask_tag);
     wait_copies();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < jfull; j += 2) {
+    step(j, sK0, sV0, sK1, sV1, Full());
+    step(j + 1, sK1, sV1, sK0, sV0, Full());
+  }
+  for (; j < nt; j += 2) {
+    if (j < jfull) step(j, sK0, sV0, sK1, sV1, Full());
+    else step(j, sK0, sV0, sK1, sV1, Any());
     if (j + 1 >= nt) break;
-    if (j + 2 < nt) {
-      tile_to_lds<T, D, kKTile, kWaves>(rK, sK0, (j + 2) * kKTile, w);
-      tile_to_lds<T, D, kKTile, kWaves>(rV, sV0, (j + 2) * kKTile, w);
-    }
-    tile(sK1, sV1, (j + 1) * kKTile);
-    wait_copies();
-    __syncthreads();
+    step(j + 1, sK1, sV1, sK0, sV0, Any());
   }
 
   store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);

@@ -186,20 +186,6 @@ __device__ __forceinline__ void frag_col(f32x8& f, const char* s, int rA, int rB
   }
 }
 
-// Eight fp32 values of a D-register block as a k16 fragment.
-__device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = (bf16)s[base + j];
-}
-__device__ __forceinline__ void frag_from(f16x8& f, const f32x16& s, int base) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = (f16)s[base + j];
-}
-__device__ __forceinline__ void frag_from(f32x8& f, const f32x16& s, int base) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = s[base + j];
-}
-
 // bf16 -> fp16 conversion of the 1 KB LDS chunks [c0, c0 + n) of `src` into
 // the same positions of `dst` (one 16-byte granule per lane and chunk).  Exact
 // for |x| in [2^-14, 65504]; smaller magnitudes keep an absolute error below
@@ -215,11 +201,128 @@ __device__ __forceinline__ void lds_bf16_to_f16(const char* src, char* dst, int 
   }
 }
 
+// ---------------------------------------------------------------- precomputed addressing
+// The granule permutation of a row depends only on the row index modulo 16, so
+// the per-lane part of every fragment address can be computed once per kernel;
+// what varies per fragment (row block, k-step, tile buffer) is then a
+// compile-time constant that the LDS instructions take as an immediate offset.
+template <typename T, int D>
+struct RowFrags {
+  // Row fragment (rb, ks): row 32 rb + lane % 32, columns 16 ks + 8 (lane / 32) .. + 7.
+  int off[D / 16];
+  __device__ __forceinline__ void init() {
+    const int l = lane_id();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = Lay<T, D>::off(l & 31, 16 * ks + 8 * (l >> 5));
+  }
+  __device__ __forceinline__ void read(bf16x8& f, const char* tile, int rb, int ks) const {
+    f = *reinterpret_cast<const bf16x8*>(tile + rb * 32 * Lay<T, D>::RB + off[ks]);
+  }
+  __device__ __forceinline__ void read(f32x8& f, const char* tile, int rb, int ks) const {
+    const char* p = tile + rb * 32 * Lay<T, D>::RB + off[ks];
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 16);
+    f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
+template <typename T, int D>
+struct ColFrags {
+  // Column fragment (t, db): rows 32 (t / 2) + 16 (t % 2) + 4 (lane / 32) + e (registers
+  // e = 0..3) and the same + 8 (registers 4..7), column 32 db + lane % 32.  This is the
+  // row set of register block t % 2 of a D tile's rows 32 (t / 2) .. + 31.
+  int off[2][D / 32];
+  __device__ __forceinline__ void init() {
+    const int l = lane_id();
+    const int hf = l >> 5;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        if constexpr (sizeof(T) == 2)
+          off[b][db] = Lay<T, D>::off(4 * hf + ((l & 15) >> 2) + 8 * b, 32 * db + (l & 16) + 4 * (l & 3));
+        else
+          off[b][db] = Lay<T, D>::off(4 * hf + 8 * b, 32 * db + (l & 31));
+      }
+  }
+  __device__ static __forceinline__ int row0(int t) { return (32 * (t >> 1) + 16 * (t & 1)) * Lay<T, D>::RB; }
+  template <typename V8>
+  __device__ __forceinline__ void read(V8& f, const char* tile, int t, int db) const {
+    static_assert(sizeof(T) == 2, "16-bit tiles");
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* p = tile + row0(t);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + off[0][db]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + off[1][db]));
+    f = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  __device__ __forceinline__ void read(f32x8& f, const char* tile, int t, int db) const {
+    const char* p = tile + row0(t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = *reinterpret_cast<const float*>(p + off[0][db] + e * Lay<T, D>::RB);
+      f[4 + e] = *reinterpret_cast<const float*>(p + off[1][db] + e * Lay<T, D>::RB);
+    }
+  }
+};
+
+// Global -> LDS copy of a [ROWS x D] tile split over NW waves, with the per-lane
+// source offsets precomputed.  `issue` copies rows [row0, row0 + ROWS) of the
+// [n x D] tensor at `base`; rows at or past n arrive as zeros (the buffer
+// resource of each copy starts at row0 and ends at row n).
+template <typename T, int D, int ROWS, int NW>
+struct TileCopy {
+  typedef Lay<T, D> L;
+  static constexpr int CPW = ROWS * L::RB / 1024 / NW;  // 1 KB chunks per wave
+  static_assert(CPW * NW * 1024 == ROWS * L::RB, "tile must split evenly over the waves");
+  uint32_t voff[CPW];
+  int chunk0;
+  __device__ __forceinline__ void init(int w) {
+    const int lane = lane_id();
+    constexpr int RPC = 64 / L::G;
+    chunk0 = w * CPW;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int rr = (chunk0 + i) * RPC + lane / L::G;
+      voff[i] = (uint32_t)rr * L::RB + (uint32_t)(((lane % L::G) ^ L::sw(rr)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(const T* base, int n, int row0, char* dst) const {
+    const rsrc_t r = make_rsrc(base + (size_t)row0 * D, (uint32_t)(n - row0) * (uint32_t)L::RB);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (chunk0 + i) * 1024), 16, voff[i], 0, 0, 0);
+  }
+  // bf16 -> fp16 conversion of this wave's chunks of `src` into the same positions of `dst`.
+  __device__ __forceinline__ void convert(const char* src, char* dst) const {
+    lds_bf16_to_f16(src, dst, chunk0, CPW);
+  }
+};
+
+// Eight fp32 values of a D-register block as a k16 fragment.
+__device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (bf16)s[base + j];
+}
+__device__ __forceinline__ void frag_from(f16x8& f, const f32x16& s, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (f16)s[base + j];
+}
+__device__ __forceinline__ void frag_from(f32x8& f, const f32x16& s, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = s[base + j];
+}
+
 // Zero-fills `bytes` (a multiple of 16) of LDS with NT threads.
 template <int NT>
 __device__ __forceinline__ void lds_zero(char* p, int bytes) {
   for (int o = threadIdx.x * 16; o < bytes; o += NT * 16) *reinterpret_cast<u32x4*>(p + o) = u32x4{0u, 0u, 0u, 0u};
 }
+
+// ---------------------------------------------------------------- instruction scheduling
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier: the groups
+// placed after a block of code order that block's instructions (matching
+// instructions fill the groups in order; the rest are scheduled freely).
+enum : int { kSgValu = 0x2, kSgMfma = 0x8, kSgDsRead = 0x100, kSgDsWrite = 0x200 };
+#define FA_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // ---------------------------------------------------------------- lane exchange
 // Value held by lane l ^ 32.

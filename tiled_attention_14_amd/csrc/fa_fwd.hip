@@ -40,6 +40,8 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -70,7 +72,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int TB = kBc * L::RB;         // bytes of one K or V tile
   constexpr int KS = D / 16;              // contraction steps over d
   constexpr int DB = D / 32;              // 32-wide blocks of d in the output
-  constexpr int CPW = TB / 1024 / kWaves; // 1 KB copy chunks per wave and tile
   __shared__ __attribute__((aligned(1024))) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
   __shared__ __attribute__((aligned(1024))) char sVr[kConv ? TB : 16];
 
@@ -85,8 +86,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const size_t slab = (size_t)N * D;
   const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
   const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)bh * slab, slab_bytes);
-  const rsrc_t rK = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
-  const rsrc_t rV = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab, slab_bytes);
 
   const int q0w = qt * kBr + 32 * w;  // first query row of this wave
   const int myq = q0w + l32;          // query row owned by this lane
@@ -96,6 +95,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBr) : N;
   const int nt = (kend + kBc - 1) / kBc;
+  const T* Kh = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kvh) * slab;
+  const T* Vh = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab;
+  RowFrags<T, D> rf;
+  ColFrags<T, D> cf;
+  TileCopy<T, D, kBc, kWaves> tc;
+  rf.init();
+  cf.init();
+  tc.init(w);
 
   // Zero the tiles once so that nothing read from LDS is ever uninitialised.
   lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
@@ -105,11 +112,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   // V tile j+1 is copied into the staging buffer (bf16) or straight into its
   // tile (fp32); the staging buffer is converted into the tile by the same wave.
   auto copy_kv = [&](char* sK, char* sV, int k0) {
-    tile_to_lds<T, D, kBc, kWaves>(rK, sK, k0, w);
-    tile_to_lds<T, D, kBc, kWaves>(rV, kConv ? sVr : sV, k0, w);
+    tc.issue(Kh, N, k0, sK);
+    tc.issue(Vh, N, k0, kConv ? sVr : sV);
   };
   auto finish_v = [&](char* sV) {
-    if constexpr (kConv) lds_bf16_to_f16(sVr, sV, w * CPW, CPW);
+    if constexpr (kConv) tc.convert(sVr, sV);
   };
   copy_kv(sK0, sV0, 0);
   wait_copies();
@@ -121,9 +128,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  auto tile = [&](const char* sK, const char* sV, int k0) {
-    if (CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
-    // S^T = K Q^T for this wave's 32 queries.
+  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK selects
+  // the general form (causal diagonal, ragged tail, waves with nothing to do);
+  // tiles that are full for the whole workgroup take the mask-free form.
+  auto tile = [&](const char* sK, const char* sV, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (MASK && CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -131,23 +141,23 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         F kf;
-        frag_row<D>(kf, sK, kb * 32 + l32, 16 * ks + 8 * hf);
+        rf.read(kf, sK, kb, ks);
         s[kb] = mfma_k16(kf, qf[ks], s[kb]);
       }
     }
-    // Causal mask on diagonal tiles; keys past N on the last tile.
-    if (CAUSAL ? (k0 + kBc - 1 > q0w) : (k0 + kBc > N)) {
+    if (MASK) {
+      // key > myq (causal) or key >= N: with lim = myq - k0 - 4 hf (resp. N - 1 - k0 - 4 hf)
+      // the test is a compare of lim with a per-register constant.
+      const int lim = (CAUSAL ? myq : N - 1) - k0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (CAUSAL ? key > myq : key >= N) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
     }
     float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
+    for (int i = 1; i < 16; ++i) mt = fmaxf(fmaxf(s[0][i], s[1][i]), mt);
     mt = fmaxf(mt, other_half(mt)) * a.c;
     if (__ballot(mt > m + kSlack)) {
       const float mnew = fmaxf(m, mt);
@@ -157,44 +167,53 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
-    float ps = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
         s[kb][i] = p;
-        ps += p;
+        ps[i & 3] += p;
       }
-    lsum += ps;
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
     for (int t = 0; t < kBc / 16; ++t) {
       PF pf;
       frag_from(pf, s[t >> 1], (t & 1) * 8);
-      const int rA = (t >> 1) * 32 + (t & 1) * 16 + 4 * hf;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         PF vf;
-        frag_col<D>(vf, sV, rA, rA + 8, db * 32);
+        cf.read(vf, sV, t, db);
         acc[db] = mfma_k16(vf, pf, acc[db]);
       }
     }
   };
+  typedef std::integral_constant<bool, false> Full;
+  typedef std::integral_constant<bool, true> Any;
 
-  // Two tiles per iteration so that each buffer is a distinct LDS object.
-  for (int j = 0; j < nt; j += 2) {
-    if (j + 1 < nt) copy_kv(sK1, sV1, (j + 1) * kBc);
-    tile(sK0, sV0, j * kBc);
+  // Tiles [0, jfull) are unmasked for every query of the workgroup.
+  const int jfull = min(nt, CAUSAL ? (qt * kBr) / kBc : N / kBc);
+  // Two tiles per iteration so that each buffer is a distinct LDS object;
+  // tile j+1 is copied while tile j is consumed.
+  auto step = [&](int j, char* sKc, char* sVc, char* sKn, char* sVn, auto mask_tag) {
+    if (j + 1 < nt) copy_kv(sKn, sVn, (j + 1) * kBc);
+    tile(sKc, sVc, j * kBc, mask_tag);
     wait_copies();
-    if (j + 1 < nt) finish_v(sV1);
+    if (j + 1 < nt) finish_v(sVn);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < jfull; j += 2) {
+    step(j, sK0, sV0, sK1, sV1, Full());
+    step(j + 1, sK1, sV1, sK0, sV0, Full());
+  }
+  for (; j < nt; j += 2) {
+    if (j < jfull) step(j, sK0, sV0, sK1, sV1, Full());
+    else step(j, sK0, sV0, sK1, sV1, Any());
     if (j + 1 >= nt) break;
-    if (j + 2 < nt) copy_kv(sK0, sV0, (j + 2) * kBc);
-    tile(sK1, sV1, (j + 1) * kBc);
-    wait_copies();
-    if (j + 2 < nt) finish_v(sV0);
-    __syncthreads();
+    step(j + 1, sK1, sV1, sK0, sV0, Any());
   }
 
   lsum += other_half(lsum);
