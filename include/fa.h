@@ -79,7 +79,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: two float32 per
- * query row (D_i = sum_c dO_ic * O_ic and lse_i * log2 e) and, only for GQA
+ * query row (-D_i = -sum_c dO_ic * O_ic and lse_i * log2 e) and, only for GQA
  * shapes whose query heads are spread over several workgroups of the dK/dV
  * kernel, float32 partial sums of dK and dV (at most 8 * B * H * N * d
  * bytes).  Linear in the sequence length N.  Valid for both values of
@@ -112,7 +112,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
  * does.  They exist so that callers and benchmarks can time or schedule the
  * phases separately.
  *
- * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic and lse_i * log2 e into the
+ * fa_bwd_preprocess: -D_i = -sum_c dO_ic * O_ic and lse_i * log2 e into the
  *   workspace.  Reads o, dO and lse.
  * fa_bwd_dkdv: recomputes P = exp(scale q k^T - lse) and dS = P * (dO v^T - D)
  *   and writes dv = P^T dO and dk = scale dS^T q.  Needs the preprocess.

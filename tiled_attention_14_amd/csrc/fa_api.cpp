@@ -38,12 +38,14 @@ fa_status_t check_shape(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype, f
 // heads; when that makes the heaviest workgroup much longer than the average
 // work per compute unit, or leaves compute units idle, the heads are sliced
 // and the slices' float32 partial sums are reduced afterwards.
-int dkdv_nsplit(int B, int H, int Hkv, int N, bool causal) {
+int dkdv_nsplit(int B, int H, int Hkv, int N, bool causal, fa_dtype_t dtype) {
   const int g = H / Hkv;
   if (g == 1) return 1;
-  const long nkt = (N + fa::kDkdvKeys - 1) / fa::kDkdvKeys;
-  const long nq = (N + fa::kDkdvQRows - 1) / fa::kDkdvQRows;
-  const long step = fa::kDkdvKeys / fa::kDkdvQRows;      // query tiles per key tile
+  const fa::Dtype t = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
+  const long keys = fa::dkdv_keys(t), rows = fa::dkdv_qrows(t);
+  const long nkt = (N + keys - 1) / keys;
+  const long nq = (N + rows - 1) / rows;
+  const long step = keys / rows;                          // query tiles per key tile
   const long first = nq;                                  // steps of key tile 0, per head
   const long sum = causal ? nkt * nq - step * nkt * (nkt - 1) / 2 : nkt * nq;
   const double avg = (double)B * Hkv * g * sum / kCUs;    // steps per compute unit
@@ -77,7 +79,7 @@ fa_status_t bwd_params(int B, int H, int Hkv, int N, int d, float scale, int cau
   fa_status_t st = check_shape(B, H, Hkv, N, d, dtype, scale);
   if (st != FA_OK) return st;
   *p = fa::BwdParams{};
-  p->nsplit = dkdv_nsplit(B, H, Hkv, N, causal != 0);
+  p->nsplit = dkdv_nsplit(B, H, Hkv, N, causal != 0, dtype);
   const WorkspaceLayout wl = layout(B, H, Hkv, N, d, p->nsplit);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < wl.total)
     return FA_ERR_WORKSPACE;
@@ -116,7 +118,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype) {
   if (check_shape(B, H, Hkv, N, d, dtype, 1.0f) != FA_OK) return 0;
-  const int ns = std::max(dkdv_nsplit(B, H, Hkv, N, false), dkdv_nsplit(B, H, Hkv, N, true));
+  const int ns = std::max(dkdv_nsplit(B, H, Hkv, N, false, dtype), dkdv_nsplit(B, H, Hkv, N, true, dtype));
   return layout(B, H, Hkv, N, d, ns).total;
 }
 

@@ -16,16 +16,19 @@
 // row constant D equals sum_j P_ij dP_ij because O = P V.
 //
 // Kernels (all on the caller's stream, no host synchronisation):
-//  1. fa_bwd_pre:  D = rowsum(dO * O) and lse * log2(e), one float each per
-//     query row, into the workspace;
-//  2. fa_bwd_dkdv: one workgroup per (batch, KV head, 128-key tile[, slice of
+//  1. fa_bwd_pre:  -D = -rowsum(dO * O) and lse * log2(e), one float each
+//     per query row, into the workspace (dP - D is then an addition, or the
+//     start value of a dP accumulator);
+//  2. fa_bwd_dkdv: one workgroup per (batch, KV head, key tile[, slice of
 //     the GQA group]); K/V fragments and the dK/dV accumulators stay in
-//     registers while Q/dO tiles of 64 rows stream through LDS (global -> LDS
-//     copies, double-buffered), for every query head of the group and, under
-//     the causal mask, only from the diagonal on.  No atomics: each key row is
-//     owned by one lane.  When a GQA group is sliced over several workgroups
-//     (to balance the work of very wide groups), each writes float32 partial
-//     sums and fa_bwd_reduce adds them in a fixed order;
+//     registers while Q/dO tiles stream through LDS (global -> LDS copies),
+//     for every query head of the group and, under the causal mask, only from
+//     the diagonal on.  bf16 uses 256-key tiles and pairs of waves that split
+//     the step between them (2b below); float32 uses 128-key tiles, one wave
+//     per 32 keys (2a).  No atomics: each key row is owned by one lane.  When
+//     a GQA group is sliced over several workgroups (to balance the work of
+//     very wide groups), each writes float32 partial sums and fa_bwd_reduce
+//     adds them in a fixed order;
 //  3. fa_bwd_dq:   one workgroup per (batch, head, 128-query tile); Q/dO
 //     fragments and the dQ accumulator stay in registers while K/V tiles of 64
 //     keys stream through LDS.  It recomputes S and dP instead of exchanging
@@ -93,14 +96,14 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const T* __restrict__ O
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, TPR);
   if (row < rows && c8 == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;
     lse2[row] = lse[row] * kLog2e;
   }
 }
 
-// ------------------------------------------------------------------ 2. dK / dV
-constexpr int kKeys = kDkdvKeys;    // keys per workgroup (32 per wave)
-constexpr int kQRows = kDkdvQRows;  // query rows per step
+// ------------------------------------------------------------------ 2a. dK / dV, float32
+constexpr int kKeys = kDkdvKeysF32;    // keys per workgroup (32 per wave)
+constexpr int kQRows = kDkdvQRowsF32;  // query rows per step
 static_assert(kKeys == 32 * kWaves, "one 32-key column block per wave");
 
 template <typename T, int D, bool CAUSAL>
@@ -170,8 +173,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const size_t head = (size_t)b * a.H + hq;
     tc.issue(reinterpret_cast<const T*>(a.q) + head * slab, N, qb0, bq);
     tc.issue(reinterpret_cast<const T*>(a.dO) + head * slab, N, qb0, bo);
-    if (w == 0) vec64_to_lds(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
-    if (w == 1) vec64_to_lds(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
+    if (w == 0) vec_to_lds<64>(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
+    if (w == 1) vec_to_lds<64>(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
   };
   // Steps that touch the causal diagonal or the ragged end of the sequence.
   auto masked = [&](int it) {
@@ -220,7 +223,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             if ((CAUSAL && c < lim) || c > qlim) p = 0.f;
           }
           s[mb][i] = p;
-          dp[mb][i] = p * (dp[mb][i] - dd[e]);
+          dp[mb][i] = p * (dp[mb][i] + dd[e]);
         }
       }
     };
@@ -275,7 +278,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     auto sm = [&](int mb, int i) {
       const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.c, -lv[mb][i >> 2][i & 3]));
       s[mb][i] = p;
-      dp[mb][i] = p * (dp[mb][i] - dd[mb][i >> 2][i & 3]);
+      dp[mb][i] = p * (dp[mb][i] + dd[mb][i >> 2][i & 3]);
     };
     F pf[2 * MB], dsf[2 * MB];
     auto cvt = [&](int t) {
@@ -359,9 +362,296 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_bf16(BwdArgs a) { dkdv_body<bf16, D, CAUSAL>(a); }
-template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_f32(BwdArgs a) { dkdv_body<float, D, CAUSAL>(a); }
+
+// ------------------------------------------------------------------ 2b. dK / dV, bf16: wave pairs
+// Eight waves and 256 keys per workgroup; the four wave pairs own 64 keys
+// each.  In a pair, the P wave holds the pair's K rows and computes S = Q K^T,
+// P and dV^T += dO^T P; the dS wave holds its V rows and computes dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^T dS one step behind, with P passed through
+// LDS (in fp16).  Waves w and w + 4 share a SIMD, so the exponentials of one
+// overlap the products of the other, and owning 64 keys per wave lets every Q
+// or dO fragment read from LDS feed two products (half the LDS traffic per
+// product of one 32-key block per wave).  One barrier per step: while the P
+// wave handles step i, the dS wave handles step i - 1 and the copies of step
+// i + 1 land, so the Q, dO, lse and D tiles rotate over three buffers and P
+// over two.  K/V fragments (64 registers) and the accumulators (128) of a
+// wave fill most of its 256 registers at d = 128; the P-wave loop is split
+// into dead, diagonal and mask-free parts so that no step carries a branch.
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = 64 * kPairWaves;
+constexpr int kPairKeys = kDkdvKeysBf16;
+constexpr int kPairRows = kDkdvQRowsBf16;
+static_assert(kPairKeys == 64 * (kPairWaves / 2) && kPairRows == 32, "64 keys per pair, 32-row steps");
+constexpr int kPairAhead = 1;  // fragment reads in flight ahead of their products
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
+  typedef bf16x8 F;
+  typedef Lay<bf16, D> L;
+  constexpr int TQ = kPairRows * L::RB;  // bytes of one 32-row tile
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int NCW = TQ / 1024 < kPairWaves ? TQ / 1024 : kPairWaves;  // waves that issue tile copies
+  constexpr int PB = 2 * 2 * 1024;  // P of one pair and step: 2 key blocks x 2 row groups x 1 KB
+  __shared__ __attribute__((aligned(1024))) char sQ[3][TQ], sO[3][TQ], sP[2][kPairWaves / 2][PB];
+  __shared__ __attribute__((aligned(256))) float sL[3][kPairRows], sD[3][kPairRows];
+
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int pr = w & 3;  // pair
+  const int N = a.N;
+  const int g = a.H / a.Hkv, gs = g / a.nsplit;
+  int unit, kt;
+  xcd_map(blockIdx.x, a.B * a.Hkv * a.nsplit, unit, kt);  // lowest key tiles (most work) first
+  const int bkv = unit / a.nsplit, sp = unit % a.nsplit;
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
+  const int h0 = kvh * g + sp * gs;  // first query head of this slice
+  const size_t slab = (size_t)N * D;
+  const int k0 = kt * kPairKeys;
+  const int kp = k0 + 64 * pr;  // first key of the pair
+
+  TileCopy<bf16, D, kPairRows, NCW> tc;
+  if (w < NCW) tc.init(w);
+
+  const int nqt = (N + kPairRows - 1) / kPairRows;
+  const int qstart = CAUSAL ? k0 / kPairRows : 0;
+  const int nq = nqt - qstart;
+  const int total = gs * nq;
+  auto qbase = [&](int it) { return (qstart + it % nq) * kPairRows; };
+  // Per query head, steps [0, ndead) have every query before every key of
+  // the pair (query tile qi ends at k0 + 32 qi + 31) and steps [ndead, lo)
+  // touch the causal diagonal of the workgroup.
+  const int ndead = CAUSAL ? min(nq, 2 * pr) : 0;
+  const int lo = CAUSAL ? min(nq, kPairKeys / kPairRows) : 0;
+
+  auto fetch = [&](int it, int buf) {
+    const int hq = h0 + it / nq;
+    const int qb0 = qbase(it);
+    const size_t head = (size_t)b * a.H + hq;
+    if (w < NCW) {
+      tc.issue(reinterpret_cast<const bf16*>(a.q) + head * slab, N, qb0, sQ[buf]);
+      tc.issue(reinterpret_cast<const bf16*>(a.dO) + head * slab, N, qb0, sO[buf]);
+    }
+    if (w == kPairWaves - 2) vec_to_lds<kPairRows>(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), sL[buf], qb0);
+    if (w == kPairWaves - 1) vec_to_lds<kPairRows>(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), sD[buf], qb0);
+  };
+
+  // This wave's 64 keys of K (P wave) or V (dS wave) as B fragments.
+  F kv[2][KS];
+  {
+    const bf16* src = reinterpret_cast<const bf16*>(w < 4 ? a.k : a.v) + (size_t)bkv * slab;
+    const rsrc_t r = make_rsrc(src, (uint32_t)(slab * sizeof(bf16)));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) frag_global<D>(kv[kb][s], r, kp + 32 * kb + l32, 16 * s + 8 * hf);
+  }
+  // dV^T (P wave) or dK^T (dS wave) of the pair's two 32-key blocks.
+  f32x16 acc[2][DB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[kb][i] = f32x16{};
+
+  if (total > 0) fetch(0, 0);
+  wait_copies();
+  __syncthreads();
+
+  constexpr int R = kPairAhead + 1;
+  // Per-lane fragment addressing.  A row fragment (ks) of a 32-row tile sits
+  // at rbase + ((32 ks) ^ rx); a column fragment (t, db) reads its two 4-row
+  // groups at cbase[b] + 16 t RB + ((64 db) ^ cx), b = 0, 1.  The lane terms
+  // are re-derived every step (the empty asm hides their loop invariance), so
+  // that the compiler does not keep one offset register per fragment alive.
+  const int rbase0 = l32 * L::RB;
+  const int rx0 = ((2 * 0 + hf) ^ L::sw(l32)) << 4;
+  const int e4 = (lane & 15) >> 2, gl = ((lane & 16) >> 3) + ((lane & 3) >> 1);
+  int cb0[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int row = 4 * hf + e4 + 8 * bb;
+    cb0[bb] = row * L::RB + (((gl ^ (L::sw(row) & 3))) << 4) + (lane & 1) * 8;
+  }
+  const int cx0 = (D == 128 ? e4 : ((e4 >> 1) & 1)) << 6;
+  // Row-fragment product of a 32-row tile with both key blocks:
+  // out[kb] += tile(rows 0..31, all of d) * kv[kb]^T.
+  auto rows_x_kv = [&](f32x16 (&out)[2], const char* tile) {
+    int rx = rx0;
+    asm volatile("" : "+v"(rx));
+    const char* rt = tile + rbase0;
+    auto rd = [&](F& f, int ks) { f = *reinterpret_cast<const F*>(rt + ((32 * ks) ^ rx)); };
+    F fa_[R];
+#pragma unroll
+    for (int x = 0; x < kPairAhead; ++x) rd(fa_[x], x);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + kPairAhead < KS) rd(fa_[(ks + kPairAhead) % R], ks + kPairAhead);
+      out[0] = mfma_k16(fa_[ks % R], kv[0][ks], out[0]);
+      out[1] = mfma_k16(fa_[ks % R], kv[1][ks], out[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // acc[kb]^T += tile^T * frag[kb]: column fragments of a 32-row tile times
+  // the B fragments of both key blocks (16 rows per k-step).
+  auto cols_x_frag = [&](const char* tile, const F (&fr)[2][2]) {
+    constexpr int NY = 2 * DB;
+    int cx = cx0;
+    asm volatile("" : "+v"(cx));
+    const char* c0 = tile + cb0[0];
+    const char* c1 = tile + cb0[1];
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto rd = [&](F& f, int y) {
+      const int t = y / DB, db = y % DB;
+      const int o = 16 * t * L::RB + ((64 * db) ^ cx);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(c0 + o));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(c1 + o));
+      f = __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    F ct[R];
+#pragma unroll
+    for (int y = 0; y < kPairAhead; ++y) rd(ct[y], y);
+#pragma unroll
+    for (int y = 0; y < NY; ++y) {
+      if (y + kPairAhead < NY) rd(ct[(y + kPairAhead) % R], y + kPairAhead);
+      const int t = y / DB, db = y % DB;
+      acc[0][db] = mfma_k16(ct[y % R], fr[0][t], acc[0][db]);
+      acc[1][db] = mfma_k16(ct[y % R], fr[1][t], acc[1][db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  typedef std::integral_constant<bool, false> Full;
+  typedef std::integral_constant<bool, true> Any;
+  if (w < 4) {
+    const float nic = -1.f / a.c;
+    // ---- P wave: S = Q K^T, P = exp2(S c - lse2), P -> LDS, dV^T += dO^T P.
+    auto step = [&](int it, const char* tq, const char* to, const float* tl, char* tp, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int qb0 = qbase(it);
+      // The accumulators start at -lse2 / c, so that S c - lse2 is one multiply.
+      f32x16 s[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(tl + 8 * g4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[0][4 * g4 + e] = s[1][4 * g4 + e] = lv[e] * nic;
+      }
+      // The P wave's products take priority: its exponentials then overlap
+      // the dS wave's products instead of waiting behind them.
+      __builtin_amdgcn_s_setprio(1);
+      rows_x_kv(s, tq);
+      __builtin_amdgcn_s_setprio(0);
+      // Masked when key > q, i.e. when q - qb0 - 4 hf < key - qb0 - 4 hf.
+      F pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int lim = kp + 32 * kb + l32 - qb0 - 4 * hf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(s[kb][i] * a.c);
+          if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
+          s[kb][i] = p;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          frag_from(pf[kb][t], s[kb], 8 * t);
+          f16x8 ph;  // P goes to the dS wave in fp16 (P is in [0, 1]; 11-bit significand)
+          frag_from(ph, s[kb], 8 * t);
+          *reinterpret_cast<f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16) = ph;
+        }
+      }
+      __builtin_amdgcn_s_setprio(1);
+      cols_x_frag(to, pf);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    int qc = 0, it = 0;
+    // One step; a null mask_tag only copies and synchronises (dead steps).
+    auto iter = [&](auto mask_tag) {
+      const int qn = qc == 2 ? 0 : qc + 1;
+      if (it + 1 < total) fetch(it + 1, qn);
+      if constexpr (!std::is_same<decltype(mask_tag), std::nullptr_t>::value)
+        step(it, sQ[qc], sO[qc], sL[qc], sP[it & 1][pr], mask_tag);
+      wait_copies();
+      __syncthreads();
+      qc = qn;
+      ++it;
+    };
+    // Per query head: steps entirely above the diagonal for this pair, the
+    // other steps on the causal diagonal, then the mask-free ones.  Rows past
+    // N need no mask: their dO rows are zero, so they add nothing to dV, and
+    // the dS wave's dP and D for them are zero too.
+    for (int h = 0; h < gs; ++h) {
+      for (int qi = 0; qi < ndead; ++qi) iter(nullptr);
+      for (int qi = ndead; qi < lo; ++qi) iter(Any());
+      for (int qi = lo; qi < nq; ++qi) iter(Full());
+    }
+  } else {
+    // ---- dS wave: during the interval in which the P wave handles step j + 1,
+    // dP = dO V^T - D, dS = P (dP - D) and dK^T += Q^T dS for step j.
+    auto work = [&](const char* tq, const char* to, const float* td, const char* tp) {
+      f32x16 dp[2];
+      // The accumulators start at -D (the workspace holds -D per query row).
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(td + 8 * g4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { dp[0][4 * g4 + e] = nd[e]; dp[1][4 * g4 + e] = nd[e]; }
+      }
+      rows_x_kv(dp, to);
+      F ds[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ds[kb][t][j] = (bf16)((float)pv[j] * dp[kb][8 * t + j]);
+        }
+      cols_x_frag(tq, ds);
+    };
+    // Interval 0: copies of step 1 only.
+    if (1 < total) fetch(1, 1);
+    wait_copies();
+    __syncthreads();
+    int cj = 0, j = 0;  // step j, in buffer cj = j % 3
+    auto tick = [&](bool live) {
+      const int cf2 = cj == 0 ? 2 : cj - 1;  // buffer of step j + 2
+      if (j + 2 < total) fetch(j + 2, cf2);
+      if (live) work(sQ[cj], sO[cj], sD[cj], sP[j & 1][pr]);
+      if (j + 1 < total) {
+        wait_copies();
+        __syncthreads();
+      }
+      cj = cj == 2 ? 0 : cj + 1;
+      ++j;
+    };
+    for (int h = 0; h < gs; ++h) {
+      for (int qi = 0; qi < ndead; ++qi) tick(false);
+      for (int qi = ndead; qi < nq; ++qi) tick(true);
+    }
+  }
+
+  // Lane l32 of key block kb owns key kp + 32 kb + l32.
+  const int which = w < 4 ? 1 : 0;  // 0: dK, 1: dV
+  const float sc = w < 4 ? 1.f : a.scale;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kp + 32 * kb + l32;
+    if (a.nsplit == 1) {
+      bf16* dst = reinterpret_cast<bf16*>(which ? a.dv : a.dk) + (size_t)bkv * slab;
+      store_rows<bf16, D>(dst, key, N, acc[kb], sc);
+    } else {
+      const size_t ps = (size_t)a.B * a.Hkv * slab;  // elements of one partial tensor
+      store_rows<float, D>(a.part + (2 * sp + which) * ps + (size_t)bkv * slab, key, N, acc[kb], sc);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPairThreads, 2) void fa_bwd_dkdv_kernel_bf16(BwdArgs a) {
+  dkdv_pair_body<D, CAUSAL>(a);
+}
 
 // Sums the nsplit float32 partials of dK and dV (in slice order) into dk / dv.
 template <typename T>
@@ -466,7 +756,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
         if (MASK && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
-        dp[i] = p * (dp[i] - dd);
+        dp[i] = p * (dp[i] + dd);
       }
       // dQ^T += K^T dS^T, 16 keys per step.
 #pragma unroll
@@ -531,10 +821,11 @@ hipError_t launch_pre_t(const BwdParams& p, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
   const BwdArgs a = make_args(p);
-  const int nkt = (p.N + kKeys - 1) / kKeys;
+  constexpr int keys = sizeof(T) == 2 ? kPairKeys : kKeys;
+  const int nkt = (p.N + keys - 1) / keys;
   const dim3 grid((unsigned)((long)nkt * p.B * p.Hkv * p.nsplit));
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL>), grid, dim3(kPairThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();

@@ -134,9 +134,13 @@ __device__ __forceinline__ void tile_to_lds(rsrc_t r, char* dst, int row0, int w
   }
 }
 
-// 64 consecutive floats [row0, row0 + 64) of a vector behind `r` into LDS (one wave).
-__device__ __forceinline__ void vec64_to_lds(rsrc_t r, float* dst, int row0) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(row0 + lane_id()) * 4u, 0, 0, 0);
+// NF (32 or 64) consecutive floats [row0, row0 + NF) of a vector behind `r`
+// into LDS, issued by one wave (lanes past NF copy nothing).
+template <int NF>
+__device__ __forceinline__ void vec_to_lds(rsrc_t r, float* dst, int row0) {
+  static_assert(NF == 32 || NF == 64, "one copy instruction per vector");
+  if (NF == 64 || lane_id() < NF)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(row0 + lane_id()) * 4u, 0, 0, 0);
 }
 
 // Waits until this wave's outstanding global -> LDS copies have landed.

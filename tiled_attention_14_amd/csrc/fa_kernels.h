@@ -8,9 +8,12 @@ namespace fa {
 
 enum Dtype { kBF16 = 0, kF32 = 1 };
 
-// Key rows per workgroup of the dK/dV kernel and query rows per step of its loop.
-constexpr int kDkdvKeys = 128;
-constexpr int kDkdvQRows = 64;
+// Key rows per workgroup of the dK/dV kernel and query rows per step of its
+// loop: bf16 runs the eight-wave pair kernel, float32 the four-wave one.
+constexpr int kDkdvKeysBf16 = 256, kDkdvQRowsBf16 = 32;
+constexpr int kDkdvKeysF32 = 128, kDkdvQRowsF32 = 64;
+inline int dkdv_keys(Dtype t) { return t == kBF16 ? kDkdvKeysBf16 : kDkdvKeysF32; }
+inline int dkdv_qrows(Dtype t) { return t == kBF16 ? kDkdvQRowsBf16 : kDkdvQRowsF32; }
 
 struct FwdParams {
   const void* q; const void* k; const void* v;
@@ -25,7 +28,7 @@ struct BwdParams {
   const void* q; const void* k; const void* v;
   const void* o; const void* dO; const float* lse;
   void* dq; void* dk; void* dv;
-  float* delta;   // [B, H, N] workspace: D_i = sum_c dO_ic O_ic
+  float* delta;   // [B, H, N] workspace: -D_i = -sum_c dO_ic O_ic
   float* lse2;    // [B, H, N] workspace: lse_i * log2(e)
   float* part;    // [nsplit, 2, B, Hkv, N, d] float32 partial dK / dV (nsplit > 1 only)
   int nsplit;     // query-head slices of a GQA group handled by separate workgroups
