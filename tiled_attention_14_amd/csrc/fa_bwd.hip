@@ -368,16 +368,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_f32(BwdArgs a)
 // Eight waves and 256 keys per workgroup; the four wave pairs own 64 keys
 // each.  In a pair, the P wave holds the pair's K rows and computes S = Q K^T,
 // P and dV^T += dO^T P; the dS wave holds its V rows and computes dP = dO V^T,
-// dS = P (dP - D) and dK^T += Q^T dS one step behind, with P passed through
-// LDS (in fp16).  Waves w and w + 4 share a SIMD, so the exponentials of one
-// overlap the products of the other, and owning 64 keys per wave lets every Q
-// or dO fragment read from LDS feed two products (half the LDS traffic per
-// product of one 32-key block per wave).  One barrier per step: while the P
-// wave handles step i, the dS wave handles step i - 1 and the copies of step
-// i + 1 land, so the Q, dO, lse and D tiles rotate over three buffers and P
-// over two.  K/V fragments (64 registers) and the accumulators (128) of a
-// wave fill most of its 256 registers at d = 128; the P-wave loop is split
-// into dead, diagonal and mask-free parts so that no step carries a branch.
+// dS = P (dP - D) and dK^T += Q^T dS, with P passed through LDS (in fp16).
+// Waves w and w + 4 share a SIMD, so the exponentials of one overlap the
+// products of the other, and owning 64 keys per wave lets every Q or dO
+// fragment read from LDS feed two products (half the LDS traffic per product
+// of one 32-key block per wave).  One barrier per step: while the P wave
+// handles step i, the dS wave forms dP and dS of step i - 1 and adds the dK
+// of step i - 2 (its dS kept in registers), and the copies of step i + 1
+// land; the Q, dO, lse and D tiles rotate over four buffers and P over two.
+// K/V fragments (64 registers) and the accumulators (128) of a wave fill most
+// of its 256 registers at d = 128; the P-wave loop is split into dead,
+// diagonal and mask-free parts so that no step carries a branch.
 constexpr int kPairWaves = 8;
 constexpr int kPairThreads = 64 * kPairWaves;
 constexpr int kPairKeys = kDkdvKeysBf16;
@@ -393,8 +394,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int NCW = TQ / 1024 < kPairWaves ? TQ / 1024 : kPairWaves;  // waves that issue tile copies
   constexpr int PB = 2 * 2 * 1024;  // P of one pair and step: 2 key blocks x 2 row groups x 1 KB
-  __shared__ __attribute__((aligned(1024))) char sQ[3][TQ], sO[3][TQ], sP[2][kPairWaves / 2][PB];
-  __shared__ __attribute__((aligned(256))) float sL[3][kPairRows], sD[3][kPairRows];
+  __shared__ __attribute__((aligned(1024))) char sQ[4][TQ], sO[4][TQ], sP[2][kPairWaves / 2][PB];
+  __shared__ __attribute__((aligned(256))) float sL[4][kPairRows], sD[4][kPairRows];
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,6 +455,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[kb][i] = f32x16{};
 
+  // The dS wave's first dK multiplies a zero dS with buffer 3; keep it finite.
+  lds_zero<kPairThreads>(sQ[3], TQ);
   if (total > 0) fetch(0, 0);
   wait_copies();
   __syncthreads();
@@ -565,16 +568,21 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       cols_x_frag(to, pf);
       __builtin_amdgcn_s_setprio(0);
     };
-    int qc = 0, it = 0;
+    int it = 0;
     // One step; a null mask_tag only copies and synchronises (dead steps).
     auto iter = [&](auto mask_tag) {
-      const int qn = qc == 2 ? 0 : qc + 1;
-      if (it + 1 < total) fetch(it + 1, qn);
-      if constexpr (!std::is_same<decltype(mask_tag), std::nullptr_t>::value)
+      const int qc = it & 3;
+      if (it + 1 < total) fetch(it + 1, (it + 1) & 3);
+      if constexpr (!std::is_same<decltype(mask_tag), std::nullptr_t>::value) {
         step(it, sQ[qc], sO[qc], sL[qc], sP[it & 1][pr], mask_tag);
+      } else {
+        // P = 0 for the dS wave, which handles every step alike.
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<u32x4*>(sP[it & 1][pr] + c * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
       wait_copies();
       __syncthreads();
-      qc = qn;
       ++it;
     };
     // Per query head: steps entirely above the diagonal for this pair, the
@@ -587,9 +595,14 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       for (int qi = lo; qi < nq; ++qi) iter(Full());
     }
   } else {
-    // ---- dS wave: during the interval in which the P wave handles step j + 1,
-    // dP = dO V^T - D, dS = P (dP - D) and dK^T += Q^T dS for step j.
-    auto work = [&](const char* tq, const char* to, const float* td, const char* tp) {
+    // ---- dS wave, two steps behind the P wave: while the P wave handles
+    // step j + 1, dK^T += Q^T dS for step j - 1 (dS kept in registers from
+    // the previous interval), then dP = dO V^T - D and dS = P (dP - D) for
+    // step j.  The products of this wave thus run while the P wave computes
+    // exponentials, and its vector work while the P wave runs products.
+    F ds[2][2];
+    auto dk = [&](const char* tq) { cols_x_frag(tq, ds); };
+    auto dpds = [&](const char* to, const float* td, const char* tp) {
       f32x16 dp[2];
       // The accumulators start at -D (the workspace holds -D per query row).
 #pragma unroll
@@ -599,7 +612,6 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
         for (int e = 0; e < 4; ++e) { dp[0][4 * g4 + e] = nd[e]; dp[1][4 * g4 + e] = nd[e]; }
       }
       rows_x_kv(dp, to);
-      F ds[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -608,28 +620,28 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) ds[kb][t][j] = (bf16)((float)pv[j] * dp[kb][8 * t + j]);
         }
-      cols_x_frag(tq, ds);
     };
     // Interval 0: copies of step 1 only.
     if (1 < total) fetch(1, 1);
     wait_copies();
     __syncthreads();
-    int cj = 0, j = 0;  // step j, in buffer cj = j % 3
-    auto tick = [&](bool live) {
-      const int cf2 = cj == 0 ? 2 : cj - 1;  // buffer of step j + 2
-      if (j + 2 < total) fetch(j + 2, cf2);
-      if (live) work(sQ[cj], sO[cj], sD[cj], sP[j & 1][pr]);
+    // Every interval runs dK for step j - 1 and dP / dS for step j; steps the
+    // pair skips arrive with P = 0 (and so dS = 0), and the first dK adds the
+    // zero dS set here.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) ds[kb][t] = F{};
+    for (int j = 0; j < total; ++j) {
+      if (j + 2 < total) fetch(j + 2, (j + 2) & 3);
+      dk(sQ[(j - 1) & 3]);
+      dpds(sO[j & 3], sD[j & 3], sP[j & 1][pr]);
       if (j + 1 < total) {
         wait_copies();
         __syncthreads();
       }
-      cj = cj == 2 ? 0 : cj + 1;
-      ++j;
-    };
-    for (int h = 0; h < gs; ++h) {
-      for (int qi = 0; qi < ndead; ++qi) tick(false);
-      for (int qi = ndead; qi < nq; ++qi) tick(true);
     }
+    dk(sQ[(total - 1) & 3]);
   }
 
   // Lane l32 of key block kb owns key kp + 32 kb + l32.
