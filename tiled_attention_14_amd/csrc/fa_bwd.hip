@@ -529,43 +529,94 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   if (w < 4) {
     const float nic = -1.f / a.c;
     // ---- P wave: S = Q K^T, P = exp2(S c - lse2), P -> LDS, dV^T += dO^T P.
+    // The two key blocks are staggered so that the exponentials of one run
+    // between the products of the other:
+    //   S0 | S1 + exp(S0) | dV0 + exp(S1) | dV1
+    // (Q and dO^T fragments are read once per key block.)
     auto step = [&](int it, const char* tq, const char* to, const float* tl, char* tp, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int qb0 = qbase(it);
       // The accumulators start at -lse2 / c, so that S c - lse2 is one multiply.
-      f32x16 s[2];
+      f32x16 s0, s1;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 lv = *reinterpret_cast<const f32x4*>(tl + 8 * g4 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[0][4 * g4 + e] = s[1][4 * g4 + e] = lv[e] * nic;
+        for (int e = 0; e < 4; ++e) s0[4 * g4 + e] = s1[4 * g4 + e] = lv[e] * nic;
       }
-      // The P wave's products take priority: its exponentials then overlap
-      // the dS wave's products instead of waiting behind them.
-      __builtin_amdgcn_s_setprio(1);
-      rows_x_kv(s, tq);
-      __builtin_amdgcn_s_setprio(0);
       // Masked when key > q, i.e. when q - qb0 - 4 hf < key - qb0 - 4 hf.
-      F pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int lim = kp + 32 * kb + l32 - qb0 - 4 * hf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(s[kb][i] * a.c);
-          if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
-          s[kb][i] = p;
-        }
+      const int lim0 = kp + l32 - qb0 - 4 * hf, lim1 = lim0 + 32;
+      auto pexp = [&](f32x16& sv, int i, int lim) {
+        float p = fast_exp2(sv[i] * a.c);
+        if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
+        sv[i] = p;
+      };
+      auto emit = [&](const f32x16& sv, F (&pf)[2], int kb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          frag_from(pf[kb][t], s[kb], 8 * t);
+          frag_from(pf[t], sv, 8 * t);
           f16x8 ph;  // P goes to the dS wave in fp16 (P is in [0, 1]; 11-bit significand)
-          frag_from(ph, s[kb], 8 * t);
+          frag_from(ph, sv, 8 * t);
           *reinterpret_cast<f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16) = ph;
         }
-      }
+      };
+      int rx = rx0;
+      asm volatile("" : "+v"(rx));
+      const char* rt = tq + rbase0;
+      auto rdq = [&](F& f, int ks) { f = *reinterpret_cast<const F*>(rt + ((32 * ks) ^ rx)); };
+      int cx = cx0;
+      asm volatile("" : "+v"(cx));
+      const char* c0 = to + cb0[0];
+      const char* c1 = to + cb0[1];
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      auto rdo = [&](F& f, int y) {
+        const int t = y / DB, db = y % DB;
+        const int o = 16 * t * L::RB + ((64 * db) ^ cx);
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(c0 + o));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(c1 + o));
+        f = __builtin_bit_cast(F, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int NY = 2 * DB;
+      constexpr int EPS = 16 / KS, EPY = 16 / NY;  // exponentials per slot
+      F fr[2];
+      // S0
       __builtin_amdgcn_s_setprio(1);
-      cols_x_frag(to, pf);
+      rdq(fr[0], 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        rdq(fr[(ks + 1) & 1], (ks + 1) % KS);  // the last read starts S1
+        s0 = mfma_k16(fr[ks & 1], kv[0][ks], s0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // S1, exp(S0)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) rdq(fr[(KS + ks + 1) & 1], ks + 1);
+        s1 = mfma_k16(fr[(KS + ks) & 1], kv[1][ks], s1);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) pexp(s0, EPS * ks + e, lim0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      F pf0[2], pf1[2];
+      emit(s0, pf0, 0);
+      // dV0, exp(S1)
+      rdo(fr[0], 0);
+#pragma unroll
+      for (int y = 0; y < NY; ++y) {
+        rdo(fr[(y + 1) & 1], (y + 1) % NY);  // the last read starts dV1
+        acc[0][y % DB] = mfma_k16(fr[y & 1], pf0[y / DB], acc[0][y % DB]);
+#pragma unroll
+        for (int e = 0; e < EPY; ++e) pexp(s1, EPY * y + e, lim1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      emit(s1, pf1, 1);
+      // dV1
+#pragma unroll
+      for (int y = 0; y < NY; ++y) {
+        if (y + 1 < NY) rdo(fr[(NY + y + 1) & 1], y + 1);
+        acc[1][y % DB] = mfma_k16(fr[(NY + y) & 1], pf1[y / DB], acc[1][y % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_s_setprio(0);
     };
     int it = 0;
