@@ -479,7 +479,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   const int cx0 = (D == 128 ? e4 : ((e4 >> 1) & 1)) << 6;
   // Row-fragment product of a 32-row tile with both key blocks:
   // out[kb] += tile(rows 0..31, all of d) * kv[kb]^T.
-  auto rows_x_kv = [&](f32x16 (&out)[2], const char* tile) {
+  auto rows_x_kv = [&](f32x16 (&out)[2], const char* tile, const f32x16& init) {
     int rx = rx0;
     asm volatile("" : "+v"(rx));
     const char* rt = tile + rbase0;
@@ -490,8 +490,10 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + kPairAhead < KS) rd(fa_[(ks + kPairAhead) % R], ks + kPairAhead);
-      out[0] = mfma_k16(fa_[ks % R], kv[0][ks], out[0]);
-      out[1] = mfma_k16(fa_[ks % R], kv[1][ks], out[1]);
+      // The first product of each chain takes `init` as its addend, so the
+      // start value needs no copy into the accumulators.
+      out[0] = mfma_k16(fa_[ks % R], kv[0][ks], ks == 0 ? init : out[0]);
+      out[1] = mfma_k16(fa_[ks % R], kv[1][ks], ks == 0 ? init : out[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -537,12 +539,12 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int qb0 = qbase(it);
       // The accumulators start at -lse2 / c, so that S c - lse2 is one multiply.
-      f32x16 s0, s1;
+      f32x16 s0, s1, si;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 lv = *reinterpret_cast<const f32x4*>(tl + 8 * g4 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s0[4 * g4 + e] = s1[4 * g4 + e] = lv[e] * nic;
+        for (int e = 0; e < 4; ++e) si[4 * g4 + e] = lv[e] * nic;
       }
       // Masked when key > q, i.e. when q - qb0 - 4 hf < key - qb0 - 4 hf.
       const int lim0 = kp + l32 - qb0 - 4 * hf, lim1 = lim0 + 32;
@@ -585,14 +587,14 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         rdq(fr[(ks + 1) & 1], (ks + 1) % KS);  // the last read starts S1
-        s0 = mfma_k16(fr[ks & 1], kv[0][ks], s0);
+        s0 = mfma_k16(fr[ks & 1], kv[0][ks], ks == 0 ? si : s0);
         __builtin_amdgcn_sched_barrier(0);
       }
       // S1, exp(S0)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) rdq(fr[(KS + ks + 1) & 1], ks + 1);
-        s1 = mfma_k16(fr[(KS + ks) & 1], kv[1][ks], s1);
+        s1 = mfma_k16(fr[(KS + ks) & 1], kv[1][ks], ks == 0 ? si : s1);
 #pragma unroll
         for (int e = 0; e < EPS; ++e) pexp(s0, EPS * ks + e, lim0);
         __builtin_amdgcn_sched_barrier(0);
@@ -654,22 +656,25 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     F ds[2][2];
     auto dk = [&](const char* tq) { cols_x_frag(tq, ds); };
     auto dpds = [&](const char* to, const float* td, const char* tp) {
-      f32x16 dp[2];
+      f32x16 dp[2], nd;
       // The accumulators start at -D (the workspace holds -D per query row).
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 nd = *reinterpret_cast<const f32x4*>(td + 8 * g4 + 4 * hf);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(td + 8 * g4 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { dp[0][4 * g4 + e] = nd[e]; dp[1][4 * g4 + e] = nd[e]; }
+        for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = v[e];
       }
-      rows_x_kv(dp, to);
+      rows_x_kv(dp, to, nd);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
+          const u32x4 pv = *reinterpret_cast<const u32x4*>(tp + (2 * kb + t) * 1024 + lane * 16);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) ds[kb][t][j] = (bf16)((float)pv[j] * dp[kb][8 * t + j]);
+          for (int j = 0; j < 4; ++j) {
+            ds[kb][t][2 * j] = (bf16)mul_f16lo_f32(pv[j], dp[kb][8 * t + 2 * j]);
+            ds[kb][t][2 * j + 1] = (bf16)mul_f16hi_f32(pv[j], dp[kb][8 * t + 2 * j + 1]);
+          }
         }
     };
     // Interval 0: copies of step 1 only.
