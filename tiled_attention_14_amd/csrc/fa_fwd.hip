@@ -51,6 +51,8 @@ constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
 constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 struct FwdArgs {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
@@ -167,21 +169,42 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    PF pfs[kBc / 16];
+    if constexpr (kConv) {
+      // The row sum adds the fp16 probabilities that the product uses, two
+      // per instruction (fp32 accumulation).
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
-        s[kb][i] = p;
-        ps[i & 3] += p;
+        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
+      const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+      for (int t = 0; t < kBc / 16; ++t) {
+        frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
+        const PF& v = pfs[t];
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), ones, lsum, false);
       }
-    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    } else {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
+          s[kb][i] = p;
+          ps[i & 3] += p;
+        }
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+      for (int t = 0; t < kBc / 16; ++t) frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
+    }
     // O^T += V^T P^T, 16 keys per step.
 #pragma unroll
     for (int t = 0; t < kBc / 16; ++t) {
-      PF pf;
-      frag_from(pf, s[t >> 1], (t & 1) * 8);
+      const PF& pf = pfs[t];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         PF vf;
