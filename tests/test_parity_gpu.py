@@ -46,6 +46,31 @@ def test_small_shapes(dt, d, causal, N, heads):
     check(w, gpu, ref, "sweep", f32_scaled=True, o_floor=floor)
 
 
+# Several key tiles of every kernel (the bf16 dK/dV kernel takes 256 keys per
+# workgroup and 32 query rows per step, the others 64 or 128), ragged ends
+# that are not multiples of 32, GQA groups (sliced and unsliced) and MHA.
+MULTI_TILE = [
+    ("bf16", 128, True, 1000, (1, 4, 2)),
+    ("bf16", 128, False, 777, (2, 2, 1)),
+    ("bf16", 64, True, 777, (1, 8, 1)),
+    ("bf16", 64, False, 1000, (1, 4, 4)),
+    ("f32", 128, True, 300, (1, 4, 2)),
+    ("f32", 64, False, 520, (1, 2, 2)),
+]
+
+
+@pytest.mark.parametrize("dt,d,causal,N,heads", MULTI_TILE, ids=lambda x: str(x))
+def test_multi_tile_ragged(dt, d, causal, N, heads):
+    B, H, Hkv = heads
+    w = synth.Workload("multi_tile", B, H, Hkv, N, d, dt, causal, seed=5000 + N + d + H + causal)
+    say(f"[parity] multi-tile {dt} d={d} causal={causal} N={N} heads={heads}")
+    gpu, ref, inp = _full(w)
+    floor = None
+    if dt == "bf16":
+        floor, _ = attention_fwd_ref(inp.f64("q"), inp.f64("k"), np.abs(inp.f64("v")), w.scale, w.causal)
+    check(w, gpu, ref, "multi-tile", f32_scaled=True, o_floor=floor)
+
+
 def test_scale_not_inverse_sqrt_d():
     w = synth.Workload("odd_scale", 2, 4, 2, 150, 64, "bf16", True, seed=77)
     inp = synth.make_inputs(w)
