@@ -12,8 +12,9 @@
 // 改进2：并行化策略优化).
 //
 // Mapping onto the CDNA4 compute unit:
-//  * one workgroup = 4 wavefronts = 128 query rows; each wave owns 32 rows,
-//    whose Q fragments stay in registers for the whole kernel;
+//  * one workgroup = 8 wavefronts = 256 query rows (bf16; 4 and 128 for
+//    fp32); each wave owns 32 rows, whose Q fragments stay in registers for
+//    the whole kernel;
 //  * K/V tiles of 64 keys go global -> LDS directly (buffer loads with the LDS
 //    destination), double-buffered: the copies of tile j+1 are in flight while
 //    tile j is consumed; rows past N arrive as zeros;
@@ -45,9 +46,11 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = 32 * kWaves;  // query rows per workgroup
+// Waves per workgroup (32 query rows each).  bf16: eight waves, two per
+// SIMD, share each K/V tile, its copy and the V conversion (one workgroup per
+// CU by LDS); fp32 (more registers per wave): four.
+constexpr int kWavesBf16 = 8;
+constexpr int kWavesF32 = 4;
 constexpr int kBc = 64;           // keys per tile
 constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
 
@@ -65,8 +68,9 @@ template <typename T> struct PvFrag;
 template <> struct PvFrag<bf16> { typedef f16x8 type; };
 template <> struct PvFrag<float> { typedef f32x8 type; };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NW>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
+  constexpr int kWaves = NW, kThreads = 64 * NW, kBr = 32 * NW;
   typedef typename Frag<T>::type F;
   typedef typename PvFrag<T>::type PF;
   typedef Lay<T, D> L;
@@ -245,22 +249,27 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel_bf16(FwdArgs a) { fwd_body<bf16, D, CAUSAL>(a); }
+__global__ __launch_bounds__(64 * kWavesBf16, 2) void fa_fwd_kernel_bf16(FwdArgs a) {
+  fwd_body<bf16, D, CAUSAL, kWavesBf16>(a);
+}
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel_f32(FwdArgs a) { fwd_body<float, D, CAUSAL>(a); }
+__global__ __launch_bounds__(64 * kWavesF32, 1) void fa_fwd_kernel_f32(FwdArgs a) {
+  fwd_body<float, D, CAUSAL, kWavesF32>(a);
+}
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N;
-  a.nqt = (p.N + kBr - 1) / kBr;
+  constexpr int waves = sizeof(T) == 2 ? kWavesBf16 : kWavesF32;
+  a.nqt = (p.N + 32 * waves - 1) / (32 * waves);
   a.c = p.scale * kLog2e;
   const dim3 grid((unsigned)((long)a.nqt * p.B * p.H));
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL>), grid, dim3(64 * waves), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL>), grid, dim3(64 * waves), 0, stream, a);
   return hipGetLastError();
 }
 
