@@ -665,16 +665,18 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
         for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = v[e];
       }
       rows_x_kv(dp, to, nd);
+      // dS = P * (dP - D) as fma(P, dP - D, z) with an addend z = 0 that the
+      // compiler cannot fold away: that form selects v_fma_mix_f32, which
+      // reads the fp16 P directly (no separate conversion).
+      float z = 0.f;
+      asm volatile("" : "+v"(z));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const u32x4 pv = *reinterpret_cast<const u32x4*>(tp + (2 * kb + t) * 1024 + lane * 16);
+          const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            ds[kb][t][2 * j] = (bf16)mul_f16lo_f32(pv[j], dp[kb][8 * t + 2 * j]);
-            ds[kb][t][2 * j + 1] = (bf16)mul_f16hi_f32(pv[j], dp[kb][8 * t + 2 * j + 1]);
-          }
+          for (int j = 0; j < 8; ++j) ds[kb][t][j] = (bf16)__builtin_fmaf((float)pv[j], dp[kb][8 * t + j], z);
         }
     };
     // Interval 0: copies of step 1 only.

@@ -301,20 +301,6 @@ struct TileCopy {
   }
 };
 
-// x times the fp16 value in the low (lo) or high (hi) half of h2, in fp32
-// (v_fma_mix_f32 reads the fp16 operand directly; one instruction instead of
-// a conversion and a multiply).
-__device__ __forceinline__ float mul_f16lo_f32(uint32_t h2, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
-  return r;
-}
-__device__ __forceinline__ float mul_f16hi_f32(uint32_t h2, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
-  return r;
-}
-
 // Eight fp32 values of a D-register block as a k16 fragment.
 __device__ __forceinline__ void frag_from(bf16x8& f, const f32x16& s, int base) {
 #pragma unroll
