@@ -468,13 +468,13 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   // are re-derived every step (the empty asm hides their loop invariance), so
   // that the compiler does not keep one offset register per fragment alive.
   const int rbase0 = l32 * L::RB;
-  const int rx0 = ((2 * 0 + hf) ^ L::sw(l32)) << 4;
+  const int rx0 = (hf ^ L::sw(l32)) << 4;
   const int e4 = (lane & 15) >> 2, gl = ((lane & 16) >> 3) + ((lane & 3) >> 1);
   int cb0[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int row = 4 * hf + e4 + 8 * bb;
-    cb0[bb] = row * L::RB + (((gl ^ (L::sw(row) & 3))) << 4) + (lane & 1) * 8;
+    cb0[bb] = row * L::RB + ((gl ^ (L::sw(row) & 3)) << 4) + (lane & 1) * 8;
   }
   const int cx0 = (D == 128 ? e4 : ((e4 >> 1) & 1)) << 6;
   // Row-fragment product of a 32-row tile with both key blocks:

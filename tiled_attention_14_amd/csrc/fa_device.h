@@ -112,28 +112,6 @@ struct Lay {
   }
 };
 
-// Asynchronous copy of rows [row0, row0 + ROWS) of the row-major [*, D] tensor
-// behind `r` into the LDS tile `dst` (global -> LDS directly, no registers).
-// Rows past the end of the tensor arrive as zeros.  The NW waves of the
-// workgroup split the work; wave `w` issues its share of 1 KB transfers, each
-// lane moving one 16-byte granule to position lane of its kilobyte.
-template <typename T, int D, int ROWS, int NW>
-__device__ __forceinline__ void tile_to_lds(rsrc_t r, char* dst, int row0, int w) {
-  typedef Lay<T, D> L;
-  constexpr int CHUNKS = ROWS * L::RB / 1024;
-  static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
-  constexpr int RPC = 64 / L::G;  // rows per kilobyte
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < CHUNKS / NW; ++i) {
-    const int ch = w * (CHUNKS / NW) + i;
-    const int rr = ch * RPC + lane / L::G;
-    const int g = (lane % L::G) ^ L::sw(rr);
-    const uint32_t voff = (uint32_t)(row0 + rr) * (uint32_t)L::RB + (uint32_t)g * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + ch * 1024), 16, voff, 0, 0, 0);
-  }
-}
-
 // NF (32 or 64) consecutive floats [row0, row0 + NF) of a vector behind `r`
 // into LDS, issued by one wave (lanes past NF copy nothing).
 template <int NF>
@@ -145,50 +123,6 @@ __device__ __forceinline__ void vec_to_lds(rsrc_t r, float* dst, int row0) {
 
 // Waits until this wave's outstanding global -> LDS copies have landed.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Row fragment: elements (r, c0 .. c0+7) of an LDS tile.
-template <int D>
-__device__ __forceinline__ void frag_row(bf16x8& f, const char* s, int r, int c0) {
-  f = *reinterpret_cast<const bf16x8*>(s + Lay<bf16, D>::off(r, c0));
-}
-template <int D>
-__device__ __forceinline__ void frag_row(f32x8& f, const char* s, int r, int c0) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(s + Lay<float, D>::off(r, c0));
-  const f32x4 b = *reinterpret_cast<const f32x4*>(s + Lay<float, D>::off(r, c0 + 4));
-  f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Column fragment: the lane owning column c0 + (lane % 32) receives elements
-// (rA + e, col) in registers e = 0..3 and (rB + e, col) in registers 4 + e.
-// rA and rB may depend on the lane half.  bf16 uses the gfx950 transposing read:
-// within each 16-lane group, result lane j element e is element j % 4 of the 8
-// bytes addressed by lane 4e + j/4.
-template <int D, typename V8>
-__device__ __forceinline__ void frag_col16(V8& f, const char* s, int rA, int rB, int c0) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const int l = lane_id();
-  const int e = (l & 15) >> 2, col = c0 + (l & 16) + 4 * (l & 3);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rA + e, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + Lay<bf16, D>::off(rB + e, col)));
-  f = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-template <int D>
-__device__ __forceinline__ void frag_col(bf16x8& f, const char* s, int rA, int rB, int c0) {
-  frag_col16<D>(f, s, rA, rB, c0);
-}
-template <int D>
-__device__ __forceinline__ void frag_col(f16x8& f, const char* s, int rA, int rB, int c0) {
-  frag_col16<D>(f, s, rA, rB, c0);
-}
-template <int D>
-__device__ __forceinline__ void frag_col(f32x8& f, const char* s, int rA, int rB, int c0) {
-  const int col = c0 + (lane_id() & 31);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = *reinterpret_cast<const float*>(s + Lay<float, D>::off(rA + e, col));
-    f[4 + e] = *reinterpret_cast<const float*>(s + Lay<float, D>::off(rB + e, col));
-  }
-}
 
 // bf16 -> fp16 conversion of the 1 KB LDS chunks [c0, c0 + n) of `src` into
 // the same positions of `dst` (one 16-byte granule per lane and chunk).  Exact
@@ -229,6 +163,11 @@ struct RowFrags {
   }
 };
 
+// Column fragments use the gfx950 transposing read ds_read_b64_tr_b16: within
+// each 16-lane group, result lane j, element e is element j % 4 of the 8 bytes
+// addressed by lane 4 e + j / 4.  Each lane therefore addresses row
+// (base + (lane % 16) / 4) at the 4-column group of its result lanes, and two
+// reads (rows r and r + 8) give one k16 fragment.
 template <typename T, int D>
 struct ColFrags {
   // Column fragment (t, db): rows 32 (t / 2) + 16 (t % 2) + 4 (lane / 32) + e (registers
