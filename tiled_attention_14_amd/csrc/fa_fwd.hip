@@ -53,6 +53,11 @@ constexpr int kWavesBf16 = 8;
 constexpr int kWavesF32 = 4;
 constexpr int kBc = 64;           // keys per tile
 constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
+// bf16: a tile is first exponentiated against the running max as it stands;
+// the result is kept when every lane's share of the tile's row sum is at most
+// this (so every p <= 2^15, inside fp16 range).  Otherwise the tile max is
+// taken and the tile redone.
+constexpr float kPLimit = 32768.f;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -161,37 +166,62 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
     }
-    float mt = fmaxf(s[0][0], s[1][0]);
+    // Running max: moved only when a tile raises it by more than kSlack.
+    auto raise_max = [&]() {
+      float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(fmaxf(s[0][i], s[1][i]), mt);
-    mt = fmaxf(mt, other_half(mt)) * a.c;
-    if (__ballot(mt > m + kSlack)) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-      m = mnew;
-      lsum *= alpha;
+      for (int i = 1; i < 16; ++i) mt = fmaxf(fmaxf(s[0][i], s[1][i]), mt);
+      mt = fmaxf(mt, other_half(mt)) * a.c;
+      if (__ballot(mt > m + kSlack)) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-    }
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+      }
+    };
     PF pfs[kBc / 16];
     if constexpr (kConv) {
-      // The row sum adds the fp16 probabilities that the product uses, two
-      // per instruction (fp32 accumulation).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
+      // p against the running max, packed to fp16; returns this lane's share
+      // of the tile's row sum, added from the fp16 values that the product
+      // uses, two per instruction (fp32 accumulation).
       const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+      auto probs = [&]() {
+        f32x16 ps[2];
 #pragma unroll
-      for (int t = 0; t < kBc / 16; ++t) {
-        frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
-        const PF& v = pfs[t];
-        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), ones, lsum, false);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ps[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], a.c, -m));
+        float ts = 0.f;
+#pragma unroll
+        for (int t = 0; t < kBc / 16; ++t) {
+          frag_from(pfs[t], ps[t >> 1], (t & 1) * 8);
+          const PF& v = pfs[t];
+          ts = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), ones, ts, false);
+          ts = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), ones, ts, false);
+        }
+        return ts;
+      };
+      // After the first tile the running max is finite for every row, and a
+      // tile rarely raises it by much: try it unchanged, and take the tile max
+      // only when some p would exceed kPLimit (an overflow gives inf, which
+      // fails the test too).
+      float ts = 0.f;
+      bool ok = false;
+      if (k0 != 0) {
+        ts = probs();
+        ok = !__ballot(!(ts <= kPLimit));
       }
+      if (!ok) {
+        raise_max();
+        ts = probs();
+      }
+      lsum += ts;
     } else {
+      raise_max();
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
