@@ -140,6 +140,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       frag_global<D>(kf[s], rK, mykey, 16 * s + 8 * hf);
       frag_global<D>(vf[s], rV, mykey, 16 * s + 8 * hf);
     }
+    wait_loads();
   }
 
   f32x16 dk[DB], dv[DB];
@@ -173,8 +174,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const size_t head = (size_t)b * a.H + hq;
     tc.issue(reinterpret_cast<const T*>(a.q) + head * slab, N, qb0, bq);
     tc.issue(reinterpret_cast<const T*>(a.dO) + head * slab, N, qb0, bo);
-    if (w == 0) vec_to_lds<64>(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
-    if (w == 1) vec_to_lds<64>(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
+    if (w == 0) vec_to_lds<64>(buffer_desc(a.lse2 + head * N, (uint32_t)N * 4u), bl, qb0);
+    if (w == 1) vec_to_lds<64>(buffer_desc(a.delta + head * N, (uint32_t)N * 4u), bd, qb0);
   };
   // Steps that touch the causal diagonal or the ragged end of the sequence.
   auto masked = [&](int it) {
@@ -384,7 +385,7 @@ constexpr int kPairThreads = 64 * kPairWaves;
 constexpr int kPairKeys = kDkdvKeysBf16;
 constexpr int kPairRows = kDkdvQRowsBf16;
 static_assert(kPairKeys == 64 * (kPairWaves / 2) && kPairRows == 32, "64 keys per pair, 32-row steps");
-constexpr int kPairAhead = 1;  // fragment reads in flight ahead of their products
+constexpr int kPairAhead = 2;  // fragment reads in flight ahead of their products
 
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
@@ -434,8 +435,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       tc.issue(reinterpret_cast<const bf16*>(a.q) + head * slab, N, qb0, sQ[buf]);
       tc.issue(reinterpret_cast<const bf16*>(a.dO) + head * slab, N, qb0, sO[buf]);
     }
-    if (w == kPairWaves - 2) vec_to_lds<kPairRows>(make_rsrc(a.lse2 + head * N, (uint32_t)N * 4u), sL[buf], qb0);
-    if (w == kPairWaves - 1) vec_to_lds<kPairRows>(make_rsrc(a.delta + head * N, (uint32_t)N * 4u), sD[buf], qb0);
+    if (w == kPairWaves - 2) vec_to_lds<kPairRows>(buffer_desc(a.lse2 + head * N, (uint32_t)N * 4u), sL[buf], qb0);
+    if (w == kPairWaves - 1) vec_to_lds<kPairRows>(buffer_desc(a.delta + head * N, (uint32_t)N * 4u), sD[buf], qb0);
   };
 
   // This wave's 64 keys of K (P wave) or V (dS wave) as B fragments.
@@ -447,6 +448,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < KS; ++s) frag_global<D>(kv[kb][s], r, kp + 32 * kb + l32, 16 * s + 8 * hf);
+    wait_loads();
   }
   // dV^T (P wave) or dK^T (dS wave) of the pair's two 32-key blocks.
   f32x16 acc[2][DB];
@@ -773,6 +775,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     }
     l2 = load4f(make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
     dd = load4f(make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
+    wait_loads();
   }
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kQTile) : N;

@@ -112,17 +112,48 @@ struct Lay {
   }
 };
 
-// NF (32 or 64) consecutive floats [row0, row0 + NF) of a vector behind `r`
-// into LDS, issued by one wave (lanes past NF copy nothing).
+// Global -> LDS copies (buffer_load ... lds): lane i's 4 or 16 bytes at
+// `voff` in the buffer land at lds + 4 i or lds + 16 i.  They are issued as
+// inline assembly so that the compiler does not track them: it cannot tell the
+// slots of a tile ring apart and would otherwise wait for every copy in flight
+// before the next read of any slot.  Each kernel waits explicitly
+// (wait_copies) and then synchronises before it reads what it copied.
+// Both operands are wave-uniform by construction; readfirstlane moves them to
+// scalar registers where the compiler computed them in vector registers.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+__device__ __forceinline__ void copy16_to_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc) : "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc) : "m0");
+}
+
+// NF (32 or 64) consecutive floats [row0, row0 + NF) of the vector behind
+// `desc` into LDS, issued by one wave (lanes past NF copy nothing).
 template <int NF>
-__device__ __forceinline__ void vec_to_lds(rsrc_t r, float* dst, int row0) {
+__device__ __forceinline__ void vec_to_lds(const u32x4& desc, float* dst, int row0) {
   static_assert(NF == 32 || NF == 64, "one copy instruction per vector");
-  if (NF == 64 || lane_id() < NF)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (uint32_t)(row0 + lane_id()) * 4u, 0, 0, 0);
+  if (NF == 64 || lane_id() < NF) copy4_to_lds(desc, (uint32_t)(row0 + lane_id()) * 4u, lds_addr(dst));
 }
 
 // Waits until this wave's outstanding global -> LDS copies have landed.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits for this wave's global loads to registers.  Called after the loads a
+// kernel keeps for its whole life, before its loop: the compiler's own waits
+// count only the memory operations it can see, so one left inside the loop
+// would also wait for the copies issued in the same step.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // bf16 -> fp16 conversion of the 1 KB LDS chunks [c0, c0 + n) of `src` into
 // the same positions of `dst` (one 16-byte granule per lane and chunk).  Exact
@@ -221,7 +252,7 @@ struct TileCopy {
   __device__ __forceinline__ void init(int w) {
     const int lane = lane_id();
     constexpr int RPC = 64 / L::G;
-    chunk0 = w * CPW;
+    chunk0 = __builtin_amdgcn_readfirstlane(w * CPW);
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int rr = (chunk0 + i) * RPC + lane / L::G;
@@ -229,10 +260,9 @@ struct TileCopy {
     }
   }
   __device__ __forceinline__ void issue(const T* base, int n, int row0, char* dst) const {
-    const rsrc_t r = make_rsrc(base + (size_t)row0 * D, (uint32_t)(n - row0) * (uint32_t)L::RB);
+    const u32x4 desc = buffer_desc(base + (size_t)row0 * D, (uint32_t)(n - row0) * (uint32_t)L::RB);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (chunk0 + i) * 1024), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < CPW; ++i) copy16_to_lds(desc, voff[i], lds_addr(dst) + (uint32_t)(chunk0 + i) * 1024u);
   }
   // bf16 -> fp16 conversion of this wave's chunks of `src` into the same positions of `dst`.
   __device__ __forceinline__ void convert(const char* src, char* dst) const {

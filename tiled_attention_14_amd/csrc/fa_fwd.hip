@@ -103,6 +103,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   F qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
+  wait_loads();
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBr) : N;
   const int nt = (kend + kBc - 1) / kBc;
