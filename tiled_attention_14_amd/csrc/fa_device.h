@@ -155,21 +155,6 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 // would also wait for the copies issued in the same step.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// bf16 -> fp16 conversion of the 1 KB LDS chunks [c0, c0 + n) of `src` into
-// the same positions of `dst` (one 16-byte granule per lane and chunk).  Exact
-// for |x| in [2^-14, 65504]; smaller magnitudes keep an absolute error below
-// 2^-25.
-__device__ __forceinline__ void lds_bf16_to_f16(const char* src, char* dst, int c0, int n) {
-  const int lane = lane_id();
-  for (int c = c0; c < c0 + n; ++c) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + c * 1024 + lane * 16);
-    f16x8 y;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = (f16)(float)x[j];
-    *reinterpret_cast<f16x8*>(dst + c * 1024 + lane * 16) = y;
-  }
-}
-
 // ---------------------------------------------------------------- precomputed addressing
 // The granule permutation of a row depends only on the row index modulo 16, so
 // the per-lane part of every fragment address can be computed once per kernel;
@@ -264,9 +249,26 @@ struct TileCopy {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) copy16_to_lds(desc, voff[i], lds_addr(dst) + (uint32_t)(chunk0 + i) * 1024u);
   }
-  // bf16 -> fp16 conversion of this wave's chunks of `src` into the same positions of `dst`.
-  __device__ __forceinline__ void convert(const char* src, char* dst) const {
-    lds_bf16_to_f16(src, dst, chunk0, CPW);
+  // Register path for bf16 tiles consumed as fp16: `load` fetches this wave's
+  // chunks of the same rows into registers (zero past n); `store_f16` converts
+  // them and writes them to the same tile positions that `issue` fills.  The
+  // conversion is exact for |x| in [2^-14, 65504]; smaller magnitudes keep an
+  // absolute error below 2^-25.
+  __device__ __forceinline__ void load(const T* base, int n, int row0, u32x4 (&r)[CPW]) const {
+    const rsrc_t rs = make_rsrc(base + (size_t)row0 * D, (uint32_t)(n - row0) * (uint32_t)L::RB);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) r[i] = load16(rs, voff[i]);
+  }
+  __device__ __forceinline__ void store_f16(const u32x4 (&r)[CPW], char* dst) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, r[i]);
+      f16x8 y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (f16)(float)x[j];
+      *reinterpret_cast<f16x8*>(dst + (chunk0 + i) * 1024 + lane * 16) = y;
+    }
   }
 };
 

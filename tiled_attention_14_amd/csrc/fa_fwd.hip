@@ -28,14 +28,16 @@
 //    accumulation): fp16 keeps 3 more significand bits than bf16, which bounds
 //    the error of O before its final bf16 rounding by about 2^-12 |O| instead
 //    of 2^-9 |O|, so that peaked rows of long sequences stay within 1e-2 after
-//    that rounding.  Each wave converts the part of the V tile it copied
-//    itself (bf16 staging buffer -> fp16 tile), so the conversion needs no
-//    extra barrier;
+//    that rounding.  Each wave loads its part of the next V tile into
+//    registers at the start of a step and writes it, converted, to the fp16
+//    tile before the step's barrier, so the conversion needs no extra barrier;
 //  * softmax runs in the log2 domain, p = exp2(s * scale*log2(e) - m), and the
 //    running maximum is only moved when a tile raises it by more than 2^8:
 //    any reference point gives the same O = acc / l and lse = m + log2(l), so
-//    skipping small moves saves the accumulator rescale on most tiles while
-//    keeping every p <= 256 (far inside the fp16 range);
+//    skipping small moves saves the accumulator rescale on most tiles.  For
+//    bf16, tiles after the first are exponentiated against the running max as
+//    it stands and kept when no p exceeds 2^15 (inside the fp16 range); only
+//    otherwise is the tile max taken and the tile redone;
 //  * workgroups of one (batch, head) share an XCD (and its L2), and under the
 //    causal mask the longest query tiles are dispatched first.
 #include "fa_device.h"
@@ -84,7 +86,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int KS = D / 16;              // contraction steps over d
   constexpr int DB = D / 32;              // 32-wide blocks of d in the output
   __shared__ __attribute__((aligned(1024))) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
-  __shared__ __attribute__((aligned(1024))) char sVr[kConv ? TB : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -119,16 +120,18 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   // Zero the tiles once so that nothing read from LDS is ever uninitialised.
   lds_zero<kThreads>(sK0, TB); lds_zero<kThreads>(sK1, TB);
   lds_zero<kThreads>(sV0, TB); lds_zero<kThreads>(sV1, TB);
-  if constexpr (kConv) lds_zero<kThreads>(sVr, TB);
   __syncthreads();
-  // V tile j+1 is copied into the staging buffer (bf16) or straight into its
-  // tile (fp32); the staging buffer is converted into the tile by the same wave.
+  // K tile j+1 is copied straight into its buffer.  V tile j+1 goes the same
+  // way for fp32; bf16 V is loaded into registers at the start of the step and
+  // written to its buffer as fp16 at the end (no staging copy in LDS).
+  u32x4 vr[TileCopy<T, D, kBc, kWaves>::CPW];
   auto copy_kv = [&](char* sK, char* sV, int k0) {
     tc.issue(Kh, N, k0, sK);
-    tc.issue(Vh, N, k0, kConv ? sVr : sV);
+    if constexpr (kConv) tc.load(Vh, N, k0, vr);
+    else tc.issue(Vh, N, k0, sV);
   };
   auto finish_v = [&](char* sV) {
-    if constexpr (kConv) tc.convert(sVr, sV);
+    if constexpr (kConv) tc.store_f16(vr, sV);
   };
   copy_kv(sK0, sV0, 0);
   wait_copies();
