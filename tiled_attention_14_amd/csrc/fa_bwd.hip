@@ -740,11 +740,14 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ 3. dQ
-constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
+// Waves (32 query rows each) per dQ workgroup: bf16 eight, two per SIMD, so
+// that each K/V tile copy serves 256 query rows; fp32 kWaves.
+constexpr int kDqWavesBf16 = 8;
 constexpr int kKTile = 64;           // keys per streamed tile
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NW>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
+  constexpr int kQTile = 32 * NW, kThreads = 64 * NW;
   typedef typename Frag<T>::type F;
   typedef Lay<T, D> L;
   constexpr int TB = kKTile * L::RB;
@@ -784,7 +787,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   const T* Vh = reinterpret_cast<const T*>(a.v) + (size_t)(b * a.Hkv + kvh) * slab;
   RowFrags<T, D> rf;
   ColFrags<T, D> cf;
-  TileCopy<T, D, kKTile, kWaves> tc;
+  TileCopy<T, D, kKTile, NW> tc;
   rf.init();
   cf.init();
   tc.init(w);
@@ -873,12 +876,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
-  dq_body<bf16, D, CAUSAL>(a, nqt);
+__global__ __launch_bounds__(64 * kDqWavesBf16, 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
+  dq_body<bf16, D, CAUSAL, kDqWavesBf16>(a, nqt);
 }
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel_f32(BwdArgs a, int nqt) {
-  dq_body<float, D, CAUSAL>(a, nqt);
+  dq_body<float, D, CAUSAL, kWaves>(a, nqt);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -912,10 +915,11 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
   const BwdArgs a = make_args(p);
-  const int nqt = (p.N + kQTile - 1) / kQTile;
+  const int qtile = 32 * (sizeof(T) == 2 ? kDqWavesBf16 : kWaves);
+  const int nqt = (p.N + qtile - 1) / qtile;
   const dim3 grid((unsigned)((long)nqt * p.B * p.H));
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a, nqt);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
   else
     hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a, nqt);
   return hipGetLastError();
