@@ -135,6 +135,61 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       float scale, int causal, fa_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Attention over a key/value cache: Nq query rows against Nk keys.
+ *
+ *   q, o : [B, H, Nq, d]    k, v : [B, Hkv, Nk, d]    lse : [B, H, Nq] float32
+ *
+ * Same conventions as fa_fwd (device pointers, GQA mapping, d, dtype, scale,
+ * lse, ownership, errors), except for the mask: `causal` != 0 aligns it at the
+ * bottom right, key j is visible to query i iff j <= i + (Nk - Nq), so the
+ * last query row sees the whole cache (decoding Nq new tokens against Nk
+ * cached ones, of which they are the last; Nq == Nk is fa_fwd's square mask).
+ * Causal calls need Nq <= Nk.  Nq = 1 is decoding one token.
+ *
+ * The keys are split into `nsplit` ranges of equal length (a multiple of 64;
+ * 0 lets the library choose from the sizes, at least 256 keys per range and
+ * enough workgroups to fill the GPU), each processed by its own workgroups,
+ * which write float32 partial results (O over the range, normalised over the
+ * range, and the range's log-sum-exp) into `workspace`; fa_merge then
+ * combines them into o and lse on the same stream.  The partials are the
+ * per-block results of the incremental softmax of "FlashAttention 在昇腾NPU上到底
+ * 快在哪", section 三、增量 Softmax, the merge its correction step, here across
+ * workgroups: short query blocks (the cache reuse of section 七 of the same
+ * page) get their parallelism from the keys.
+ *
+ * `workspace`: device memory of at least fa_fwd_splitkv_workspace_size(...)
+ * bytes for the same sizes and nsplit, 256-byte aligned, owned by the caller;
+ * contents on entry do not matter.  Returns FA_ERR_WORKSPACE when it is
+ * missing, misaligned or too small, FA_ERR_INVALID_ARG for causal calls with
+ * Nq > Nk, nsplit < 0 or sizes out of range.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype_t dtype, int nsplit);
+
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d,
+                           float scale, int causal, fa_dtype_t dtype, int nsplit,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Merge of attention results computed over disjoint key ranges (on this
+ * device by fa_fwd_splitkv, or elsewhere, e.g. one range per device of a
+ * sequence-sharded cache):
+ *
+ *   o_parts   : [nsplit, rows, d] float32, each range's output normalised over the range
+ *   lse_parts : [nsplit, rows]    float32, each range's log-sum-exp (-inf: the range
+ *                                  holds no key visible to the row; its o_parts row is ignored)
+ *   o         : [rows, d]  dtype          lse : [rows] float32
+ *
+ * lse = log sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s, i.e. the
+ * attention over the union of the ranges.  A row with lse_s = -inf in every
+ * range gets o = 0, lse = -inf.  All pointers are 16-byte aligned device
+ * pointers; nsplit >= 1, rows >= 1, d in {64, 128}.
+ */
+fa_status_t fa_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                     int nsplit, long rows, int d, fa_dtype_t dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status_t s);
 

@@ -30,7 +30,7 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess", "fa_bwd_workspace_size",
-                     "fa_fwd", "fa_status_string"]
+                     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge", "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -171,3 +171,63 @@ def test_workspace_size_is_linear_in_n(lib):
         assert b <= 2 * a + 512, (H, Hkv, a, b)
     assert fa.fa_bwd_workspace_size(0, 1, 1, 1, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 1, 1, 80, fa.FA_BF16) == 0
+
+
+# ------------------------------------------------------------------ key/value-cache forward and merge
+KV = dict(B=2, H=8, Hkv=2, Nq=3, Nk=500, d=128, scale=0.09, causal=1, dtype=fa.FA_BF16, nsplit=0)
+
+
+def _splitkv(**kw):
+    a = dict(KV); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 5)
+    ws = a.pop("ws", P)
+    wsb = a.pop("wsb", 1 << 40)
+    return fa.fa_fwd_splitkv(*ptrs, a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                             a["dtype"], a["nsplit"], ws, wsb, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=501), fa.FA_ERR_INVALID_ARG),            # causal needs Nq <= Nk
+    (dict(nsplit=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(H=7), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws=P + 16), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=1024), fa.FA_ERR_WORKSPACE),
+    (dict(ptrs=[P, P, None, P, P]), fa.FA_ERR_INVALID_ARG),
+    (dict(ptrs=[P, P, P, P + 4, P]), fa.FA_ERR_INVALID_ARG),
+])
+def test_splitkv_invalid_arguments(lib, kw, status):
+    assert _splitkv(**kw) == status
+
+
+def test_splitkv_workspace_size(lib):
+    a = KV
+    # Two float32 per row and range plus the outputs: one range per 64-key tile at most.
+    n1 = fa.fa_fwd_splitkv_workspace_size(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["dtype"], 1)
+    assert n1 >= a["B"] * a["H"] * a["Nq"] * (a["d"] + 1) * 4
+    n4 = fa.fa_fwd_splitkv_workspace_size(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["dtype"], 4)
+    assert n4 >= 4 * a["B"] * a["H"] * a["Nq"] * (a["d"] + 1) * 4
+    big = fa.fa_fwd_splitkv_workspace_size(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["dtype"], 10 ** 6)
+    assert big == fa.fa_fwd_splitkv_workspace_size(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["dtype"], 8)
+    assert fa.fa_fwd_splitkv_workspace_size(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], 96, a["dtype"], 0) == 0
+    # A workspace one byte short is rejected before anything is launched.
+    assert _splitkv(nsplit=4, wsb=n4 - 1) == fa.FA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(nsplit=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(ptrs=[P, None, P, P]), fa.FA_ERR_INVALID_ARG),
+    (dict(ptrs=[P, P, P + 2, P]), fa.FA_ERR_INVALID_ARG),
+])
+def test_merge_invalid_arguments(lib, args, status):
+    a = dict(nsplit=3, rows=10, d=64, dtype=fa.FA_F32, ptrs=[P] * 4)
+    a.update(args)
+    assert fa.fa_merge(*a["ptrs"], a["nsplit"], a["rows"], a["d"], a["dtype"], 0) == status

@@ -93,6 +93,44 @@ fa_status_t bwd_params(int B, int H, int Hkv, int N, int d, float scale, int cau
   return FA_OK;
 }
 
+// Key ranges of the split forward: enough (batch, KV head, row block, range)
+// workgroups to cover the compute units twice, ranges of at least 256 keys.
+int splitkv_auto(int B, int H, int Hkv, int Nq, int Nk) {
+  const long nrb = ((long)(H / Hkv) * Nq + 127) / 128;
+  const long base = nrb * B * Hkv;
+  const long want = (long)(2 * kCUs + base - 1) / base;
+  const long most = std::max<long>(1, Nk / 256);
+  return (int)std::max<long>(1, std::min<long>(want, std::min<long>(most, 1024)));
+}
+
+// Range length (a multiple of the 64-key tile) and the number of non-empty
+// ranges for a requested count (0 = chosen by the library).
+void splitkv_ranges(int B, int H, int Hkv, int Nq, int Nk, int nsplit, int* len, int* count) {
+  const int want = nsplit > 0 ? nsplit : splitkv_auto(B, H, Hkv, Nq, Nk);
+  const int per = (Nk + want - 1) / want;
+  *len = (per + 63) / 64 * 64;
+  *count = (Nk + *len - 1) / *len;
+}
+
+fa_status_t check_splitkv(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, fa_dtype_t dtype,
+                          int nsplit) {
+  if (Nq < 1 || nsplit < 0) return FA_ERR_INVALID_ARG;
+  fa_status_t st = check_shape(B, H, Hkv, Nk, d, dtype, scale);
+  if (st != FA_OK) return st;
+  if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+  int len, count;
+  splitkv_ranges(B, H, Hkv, Nq, Nk, nsplit, &len, &count);
+  if ((double)count * B * H * Nq >= 2147483647.0) return FA_ERR_INVALID_ARG;
+  if ((double)B * H * Nq * d >= 1099511627776.0) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t splitkv_bytes(int B, int H, int Nq, int d, int count, size_t* lse_off) {
+  const size_t rows = (size_t)count * B * H * Nq;
+  *lse_off = round_up(rows * d * sizeof(float), kAlign);
+  return *lse_off + round_up(rows * sizeof(float), kAlign);
+}
+
 bool all_aligned(std::initializer_list<const void*> ps) {
   for (const void* x : ps)
     if (!x || !aligned16(x)) return false;
@@ -166,6 +204,54 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, fa_dtype_t dtype, int nsplit) {
+  if (check_splitkv(B, H, Hkv, Nq, Nk, d, 1.0f, 0, dtype, nsplit) != FA_OK) return 0;
+  int len, count;
+  splitkv_ranges(B, H, Hkv, Nq, Nk, nsplit, &len, &count);
+  size_t lse_off;
+  return splitkv_bytes(B, H, Nq, d, count, &lse_off);
+}
+
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                           int Nq, int Nk, int d, float scale, int causal, fa_dtype_t dtype, int nsplit,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!all_aligned({q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
+  fa_status_t st = check_splitkv(B, H, Hkv, Nq, Nk, d, scale, causal, dtype, nsplit);
+  if (st != FA_OK) return st;
+  int len, count;
+  splitkv_ranges(B, H, Hkv, Nq, Nk, nsplit, &len, &count);
+  size_t lse_off;
+  const size_t need = splitkv_bytes(B, H, Nq, d, count, &lse_off);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < need)
+    return FA_ERR_WORKSPACE;
+  fa::SplitParams p;
+  p.q = q; p.k = k; p.v = v;
+  p.opart = static_cast<float*>(workspace);
+  p.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+  p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d;
+  p.nsplit = count; p.split_len = len;
+  p.scale = scale; p.causal = causal != 0;
+  p.dtype = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
+  if (fa::launch_fwd_split(p, stream) != hipSuccess) return FA_ERR_HIP;
+  fa::MergeParams mp;
+  mp.opart = p.opart; mp.lpart = p.lpart; mp.o = o; mp.lse = lse;
+  mp.rows = (long)B * H * Nq; mp.nsplit = count; mp.d = d; mp.dtype = p.dtype;
+  return fa::launch_merge(mp, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int nsplit, long rows, int d,
+                     fa_dtype_t dtype, hipStream_t stream) {
+  if (!all_aligned({o_parts, lse_parts, o, lse})) return FA_ERR_INVALID_ARG;
+  if (nsplit < 1 || rows < 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((double)rows * (d / 4) >= 549755813888.0) return FA_ERR_INVALID_ARG;
+  fa::MergeParams mp;
+  mp.opart = o_parts; mp.lpart = lse_parts; mp.o = o; mp.lse = lse;
+  mp.rows = rows; mp.nsplit = nsplit; mp.d = d; mp.dtype = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
+  return fa::launch_merge(mp, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_string(fa_status_t s) {

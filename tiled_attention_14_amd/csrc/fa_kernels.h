@@ -38,7 +38,31 @@ struct BwdParams {
   Dtype dtype;
 };
 
+// Attention of Nq query rows over Nk keys split into nsplit ranges of
+// split_len keys: float32 O [nsplit, B, H, Nq, d] and LSE [nsplit, B, H, Nq]
+// per range (bottom-right causal alignment when causal).
+struct SplitParams {
+  const void* q; const void* k; const void* v;
+  float* opart; float* lpart;
+  int B, H, Hkv, Nq, Nk, d;
+  int nsplit, split_len;
+  float scale;
+  bool causal;
+  Dtype dtype;
+};
+
+// Merge of nsplit per-range results of `rows` rows into o (dtype) and lse.
+struct MergeParams {
+  const float* opart; const float* lpart;
+  void* o; float* lse;
+  long rows;
+  int nsplit, d;
+  Dtype dtype;
+};
+
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_split(const SplitParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 // Backward phases, in stream order: preprocess (D and lse2), then the dK/dV
 // kernel (plus the reduction of its partials when nsplit > 1) and the dQ
 // kernel, which are independent of each other.

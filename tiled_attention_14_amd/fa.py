@@ -1,6 +1,7 @@
 """Thin Python binding of the C ABI in ``include/fa.h``.
 
-``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``,
+``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_workspace_size``, ``fa_merge``,
 ``fa_bwd_dq``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
 the C names and argument order; pointer arguments accept an integer device
 address or any object with ``data_ptr()`` (a torch tensor), and ``stream`` an
@@ -48,6 +49,12 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dkdv.restype = I
         L.fa_bwd_dq.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         L.fa_bwd_dq.restype = I
+        L.fa_fwd_splitkv_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        L.fa_fwd_splitkv_workspace_size.restype = S
+        L.fa_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, S, P]
+        L.fa_fwd_splitkv.restype = I
+        L.fa_merge.argtypes = [P, P, P, P, I, ctypes.c_long, I, I, P]
+        L.fa_merge.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -106,6 +113,22 @@ def fa_bwd_dq(q, k, v, dO, dq, B, H, Hkv, N, d, scale, causal, dtype,
     return lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq),
                            B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
                            _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_fwd_splitkv_workspace_size(B, H, Hkv, Nq, Nk, d, dtype, nsplit=0) -> int:
+    return lib().fa_fwd_splitkv_workspace_size(B, H, Hkv, Nq, Nk, d, int(dtype), int(nsplit))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, nsplit,
+                   workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                                float(scale), int(bool(causal)), int(dtype), int(nsplit),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_merge(o_parts, lse_parts, o, lse, nsplit, rows, d, dtype, stream=None) -> int:
+    return lib().fa_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse), int(nsplit), int(rows), d,
+                          int(dtype), _stream(stream))
 
 
 def fa_status_string(status: int) -> str:
@@ -172,3 +195,25 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None, ws=None
     if st != FA_OK:
         raise FAError(st)
     return dq, dk, dv
+
+
+def forward_kv(q, k, v, scale=None, causal=False, nsplit=0, stream=None):
+    """(o, lse) for q [B,H,Nq,d] against k/v [B,Hkv,Nk,d] through ``fa_fwd_splitkv``
+    (bottom-right causal alignment; ``nsplit`` key ranges, 0 = library's choice)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dt = FA_BF16 if q.dtype == torch.bfloat16 else FA_F32
+    s = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    n = fa_fwd_splitkv_workspace_size(B, H, Hkv, Nq, Nk, d, dt, nsplit)
+    if n == 0:
+        raise FAError(FA_ERR_INVALID_ARG)
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+    addr = (buf.data_ptr() + 255) // 256 * 256
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = fa_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, s, causal, dt, nsplit, addr, n, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse

@@ -121,3 +121,51 @@ def sample_rows(n_total: int, n_sample: int, seed: int, count: int) -> np.ndarra
     rng = np.random.Generator(np.random.PCG64(seed))
     k = min(n_sample, n_total)
     return np.stack([np.sort(rng.choice(n_total, size=k, replace=False)) for _ in range(count)])
+
+
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    """Nq query rows against a cache of Nk keys (decoding when Nq == 1)."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0) / np.sqrt(np.float32(self.d)))
+
+
+# Decoding one token per sequence against a cache, at the attention shapes of
+# the two models above: 70B-shaped GQA (64 query heads over 8 KV heads) with a
+# 8192-token cache, and 7B-shaped MHA with a 4096-token cache.
+KV_WORKLOADS = {
+    "decode_llama2_70b_gqa_b16_nk8192_d128": KvWorkload("decode_llama2_70b_gqa_b16_nk8192_d128",
+                                                        16, 64, 8, 1, 8192, 128, "bf16", True, seed=14100),
+    "decode_llama2_7b_b16_nk4096_d128": KvWorkload("decode_llama2_7b_b16_nk4096_d128",
+                                                   16, 32, 32, 1, 4096, 128, "bf16", True, seed=14101),
+}
+
+
+def make_kv_inputs(w: KvWorkload, seed: int | None = None) -> Inputs:
+    """Seeded q [B,H,Nq,d], k and v [B,Hkv,Nk,d], iid N(0,1), drawn in that
+    order like make_inputs; bf16 workloads are rounded to bf16 (RNE)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    raw = {
+        "q": rng.standard_normal((w.B, w.H, w.Nq, w.d), dtype=np.float32),
+        "k": rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32),
+        "v": rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32),
+    }
+    if w.dtype == "f32":
+        return Inputs(w, raw, None)
+    if w.dtype != "bf16":
+        raise ValueError(f"unknown dtype {w.dtype!r}")
+    bits = {n: bf16_round_bits(a) for n, a in raw.items()}
+    vals = {n: bf16_bits_to_f32(b) for n, b in bits.items()}
+    return Inputs(w, vals, bits)
