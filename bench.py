@@ -98,6 +98,53 @@ def cpu_baseline(w, inp, budget_s=12.0):
                       f"({t_total:.1f} s on the host CPU)"}
 
 
+def decode_leg(dev, calls=50, warmup=10):
+    """Times fa_fwd_splitkv (key-range kernel + merge) on the decode workloads
+    with HIP events on the launch stream.  Decoding is bound by reading the
+    cache: the rate is algorithmic bytes (q, k, v read; o, lse written) per
+    call against the HBM peak; the float32 partials are overhead, not credited."""
+    import numpy as np
+    import torch
+    from tiled_attention_14_amd import fa, synth
+    res = []
+    for name in sorted(synth.KV_WORKLOADS):
+        w = synth.KV_WORKLOADS[name]
+        inp = synth.make_kv_inputs(w)
+        t = {n: torch.from_numpy(inp.bits[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v")}
+        del inp
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        n = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, fa.FA_BF16, 0)
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        addr = (buf.data_ptr() + 255) // 256 * 256
+        stream = torch.cuda.current_stream()
+
+        def call():
+            st = fa.fa_fwd_splitkv(t["q"], t["k"], t["v"], o, lse, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.scale,
+                                   w.causal, fa.FA_BF16, 0, addr, n, stream)
+            if st != fa.FA_OK:
+                raise RuntimeError("fa_fwd_splitkv failed")
+
+        for _ in range(warmup):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(calls):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        nbytes = 2 * (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.Hkv * w.Nk * w.d) + 4 * w.B * w.H * w.Nq
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"[bench] decode {name}: {us:.1f} us per call, {gbs:.0f} GB/s")
+        res.append({"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                    "causal": w.causal, "us_per_call": round(us, 2), "bytes": nbytes, "bound": "hbm",
+                    "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        del t, o, lse, buf
+    return res
+
+
 def main():
     from tiled_attention_14_amd import synth
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -106,6 +153,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the key/value-cache decode leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -234,6 +282,7 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }
+    out["decode"] = None if args.no_decode else decode_leg(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
