@@ -11,7 +11,8 @@ are compared on every row.
 Tolerances: float32, max |gpu - ref| <= 1e-5 * max(1, max |ref|) for O and
 LSE; bfloat16, LSE max abs <= 1e-3 and O per element within
 max(1e-2, 1.05 u (attn(|V|) + |O|) + 1e-5), u = 2^-8, the bound of the
-square-attention tests (P is rounded to fp16 here, below that bound's bf16).
+square-attention tests for P and O rounded to bf16 (the decode variant, at
+most 32 rows per KV head, rounds P to bf16; the general kernel to fp16).
 """
 import numpy as np
 import pytest

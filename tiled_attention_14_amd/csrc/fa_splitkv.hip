@@ -234,6 +234,163 @@ __global__ __launch_bounds__(kSplitThreads, sizeof(T) == 2 ? 2 : 1) void fa_fwd_
   if (rvalid && hf == 0) a.lpart[pidx] = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
+// Variant for bf16 with at most 32 rows per KV head (decoding: g heads x a
+// few positions).  There the kernel is bound by reading the cache, and what
+// limits the rate is the bytes in flight per compute unit.  Tiles of 32 keys
+// rotate over kRing LDS slots for K and for V, filled by global -> LDS copies
+// issued kRing - 1 tiles ahead, so that kRing - 1 of them are in flight while
+// one is consumed (80 KB per workgroup at d = 128: two workgroups per CU).  V is
+// consumed as bf16 straight from its slot (P V on bf16 MFMA, P rounded to bf16),
+// so no V passes through registers.  Only wave 0 has rows; the other waves
+// issue their share of the copies and meet the barriers.
+constexpr int kRingKeys = 32;
+constexpr int kRing = 5;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitThreads, 2) void fa_fwd_split_ring_kernel(SplitArgs a) {
+  typedef bf16 T;
+  typedef Lay<T, D> L;
+  typedef TileCopy<T, D, kRingKeys, kSplitWaves> TC;
+  constexpr int TB = kRingKeys * L::RB;
+  constexpr int KS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char sK[kRing][TB], sV[kRing][TB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  int bid = blockIdx.x;
+  const int sp = bid % a.nsplit;
+  const int unit = bid / a.nsplit;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int g = a.H / a.Hkv;
+  const int R = g * a.Nq;                    // rows of this KV head, at most 32
+  const bool rvalid = l32 < R;
+  const int rr = rvalid ? l32 : R - 1;
+  const int h = kvh * g + rr / a.Nq, qi = rr % a.Nq;
+  const long orow = ((long)b * a.H + h) * a.Nq + qi;
+
+  const int off = a.Nk - a.Nq;
+  const int ks0 = sp * a.split_len;
+  int kend = min(a.Nk, ks0 + a.split_len);
+  if (CAUSAL) kend = min(kend, (R >= a.Nq ? a.Nq - 1 : R - 1) + off + 1);
+  const int nt = kend > ks0 ? (kend - ks0 + kRingKeys - 1) / kRingKeys : 0;
+  const int lastkey = CAUSAL ? min(kend - 1, qi + off) : kend - 1;
+  const long pidx = (long)sp * a.B * a.H * a.Nq + orow;
+
+  bf16x8 qf[KS];
+  if (w == 0) {
+    const T* qp = reinterpret_cast<const T*>(a.q) + orow * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) frag_at(qf[s], qp + 16 * s + 8 * hf);
+    wait_loads();
+  }
+  const size_t slab = (size_t)a.Nk * D;
+  const T* Kh = reinterpret_cast<const T*>(a.k) + (size_t)unit * slab;
+  const T* Vh = reinterpret_cast<const T*>(a.v) + (size_t)unit * slab;
+  RowFrags<T, D> rf;
+  ColFrags<T, D> cf;
+  TC tc;
+  rf.init();
+  cf.init();
+  tc.init(w);
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    lds_zero<kSplitThreads>(sK[i], TB);
+    lds_zero<kSplitThreads>(sV[i], TB);
+  }
+  __syncthreads();
+  auto issue = [&](int j, int slot) {
+    tc.issue(Kh, a.Nk, ks0 + j * kRingKeys, sK[slot]);
+    tc.issue(Vh, a.Nk, ks0 + j * kRingKeys, sV[slot]);
+  };
+  // Waits until tile j + 1 has landed: the copies of the tiles after it (at
+  // most kRing - 2 of them, 2 CPW instructions each) may stay in flight.
+  auto wait_next = [&](int j) {
+    const int after = min(nt - 1, j + kRing - 1) - (j + 1);
+    if (after >= 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * 2 * TC::CPW) : "memory");
+    else if (after == 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * 2 * TC::CPW) : "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * TC::CPW) : "memory");
+    else wait_copies();
+  };
+  static_assert(kRing == 5, "wait_next covers up to three tiles after the next one");
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i)
+    if (i < nt) issue(i, i);
+  wait_next(-1);
+  __syncthreads();
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  auto tile = [&](int slot, int k0) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kf;
+      rf.read(kf, sK[slot], 0, ks);
+      s = mfma_k16(kf, qf[ks], s);
+    }
+    const int lim = lastkey - k0 - 4 * hf;
+    if (lim < 27) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > lim) s[i] = -INFINITY;
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    mt = fmaxf(mt, other_half(mt)) * a.c;
+    if (__ballot(mt > m + kSplitSlack)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    bf16x8 pf[2];
+    float ts = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16 pb = (bf16)fast_exp2(__builtin_fmaf(s[8 * t + e], a.c, -mref));
+        pf[t][e] = pb;
+        ts += (float)pb;  // the row sum of the values the product uses
+      }
+    lsum += ts;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 vf;
+        cf.read(vf, sV[slot], t, db);
+        acc[db] = mfma_k16(vf, pf[t], acc[db]);
+      }
+  };
+  // Tile j sits in slot j % kRing; unrolled by kRing so that slots are fixed.
+  auto step = [&](int j, int slot) {
+    if (j + kRing - 1 < nt) issue(j + kRing - 1, (slot + kRing - 1) % kRing);
+    if (w == 0) tile(slot, ks0 + j * kRingKeys);
+    wait_next(j);
+    __syncthreads();
+  };
+  for (int j = 0; j < nt; j += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u)
+      if (j + u < nt) step(j + u, u);
+  }
+
+  if (w != 0) return;
+  lsum += other_half(lsum);
+  const bool seen = lsum > 0.f;
+  store_rows<float, D>(a.opart, (int)pidx, rvalid ? (int)pidx + 1 : (int)pidx, acc, seen ? 1.f / lsum : 0.f);
+  if (rvalid && hf == 0) a.lpart[pidx] = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
 // Merge of the ranges: one thread per 4 columns of one row.  LSE = log sum
 // exp(LSE_s) (max-subtracted), O = sum_s exp(LSE_s - LSE) O_s.
 template <typename T, int D>
@@ -270,6 +427,13 @@ hipError_t launch_split_t(const SplitParams& p, hipStream_t stream) {
   a.nsplit = p.nsplit;
   a.split_len = p.split_len;
   a.c = p.scale * kLog2e;
+  if constexpr (sizeof(T) == 2) {
+    if (p.H / p.Hkv * p.Nq <= 32) {
+      const dim3 grid((unsigned)((long)a.nsplit * p.B * p.Hkv));
+      hipLaunchKernelGGL((fa_fwd_split_ring_kernel<D, CAUSAL>), grid, dim3(kSplitThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((unsigned)((long)a.nrb * a.nsplit * p.B * p.Hkv));
   hipLaunchKernelGGL((fa_fwd_split_kernel<T, D, CAUSAL>), grid, dim3(kSplitThreads), 0, stream, a);
   return hipGetLastError();
