@@ -582,65 +582,43 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       };
       constexpr int NY = 2 * DB;
       constexpr int EPS = 16 / KS, EPY = 16 / NY;  // exponentials per slot
-      // The step's products in order: S0 (KS), S1 (KS), dV0 (NY), dV1 (NY).
-      // Each takes one A fragment from LDS (Q rows for S, dO^T columns for
-      // dV), read AH products before its use through a ring of AH + 1
-      // fragments, across the phase boundaries except the one at P0's
-      // emission.  At d = 128 the second
-      // fragment in flight costs spills that outweigh the hidden latency
-      // (same-box A/B: 70B-shaped GQA and long sequence 1.5% slower, 7B
-      // shape 3% faster); at d = 64 it is free and 13% faster.
-      constexpr int AH = D == 64 ? 2 : 1;
-      constexpr int NPW = 2 * KS + 2 * NY, RP = AH + 1;
-      F fr[RP];
-      auto rdp = [&](int y) {
-        if (y < KS) rdq(fr[y % RP], y);
-        else if (y < 2 * KS) rdq(fr[y % RP], y - KS);
-        else if (y < 2 * KS + NY) rdo(fr[y % RP], y - 2 * KS);
-        else rdo(fr[y % RP], y - 2 * KS - NY);
-      };
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int y = 0; y < AH; ++y) rdp(y);
+      F fr[2];
       // S0
+      __builtin_amdgcn_s_setprio(1);
+      rdq(fr[0], 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        rdp(ks + AH);
-        s0 = mfma_k16(fr[ks % RP], kv[0][ks], ks == 0 ? si : s0);
+        rdq(fr[(ks + 1) & 1], (ks + 1) % KS);  // the last read starts S1
+        s0 = mfma_k16(fr[ks & 1], kv[0][ks], ks == 0 ? si : s0);
         __builtin_amdgcn_sched_barrier(0);
       }
       // S1, exp(S0)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int y = KS + ks;
-        if (y + AH < 2 * KS) rdp(y + AH);
-        s1 = mfma_k16(fr[y % RP], kv[1][ks], ks == 0 ? si : s1);
+        if (ks + 1 < KS) rdq(fr[(KS + ks + 1) & 1], ks + 1);
+        s1 = mfma_k16(fr[(KS + ks) & 1], kv[1][ks], ks == 0 ? si : s1);
 #pragma unroll
         for (int e = 0; e < EPS; ++e) pexp(s0, EPS * ks + e, lim0);
         __builtin_amdgcn_sched_barrier(0);
       }
       F pf0[2], pf1[2];
       emit(s0, pf0, 0);
-      // The first dV fragments are read after P0 is emitted (none is live across it).
-#pragma unroll
-      for (int y = 2 * KS; y < 2 * KS + AH; ++y) rdp(y);
       // dV0, exp(S1)
+      rdo(fr[0], 0);
 #pragma unroll
-      for (int yy = 0; yy < NY; ++yy) {
-        const int y = 2 * KS + yy;
-        rdp(y + AH);
-        acc[0][yy % DB] = mfma_k16(fr[y % RP], pf0[yy / DB], acc[0][yy % DB]);
+      for (int y = 0; y < NY; ++y) {
+        rdo(fr[(y + 1) & 1], (y + 1) % NY);  // the last read starts dV1
+        acc[0][y % DB] = mfma_k16(fr[y & 1], pf0[y / DB], acc[0][y % DB]);
 #pragma unroll
-        for (int e = 0; e < EPY; ++e) pexp(s1, EPY * yy + e, lim1);
+        for (int e = 0; e < EPY; ++e) pexp(s1, EPY * y + e, lim1);
         __builtin_amdgcn_sched_barrier(0);
       }
       emit(s1, pf1, 1);
       // dV1
 #pragma unroll
-      for (int yy = 0; yy < NY; ++yy) {
-        const int y = 2 * KS + NY + yy;
-        if (y + AH < NPW) rdp(y + AH);
-        acc[1][yy % DB] = mfma_k16(fr[y % RP], pf1[yy / DB], acc[1][yy % DB]);
+      for (int y = 0; y < NY; ++y) {
+        if (y + 1 < NY) rdo(fr[(NY + y + 1) & 1], y + 1);
+        acc[1][y % DB] = mfma_k16(fr[(NY + y) & 1], pf1[y / DB], acc[1][y % DB]);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
