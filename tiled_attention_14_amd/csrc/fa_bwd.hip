@@ -744,7 +744,6 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restr
 // that each K/V tile copy serves 256 query rows; fp32 kWaves.
 constexpr int kDqWavesBf16 = 8;
 constexpr int kKTile = 64;           // keys per streamed tile
-constexpr int kDqAhead = 2;          // K/V fragments read ahead of their product
 
 template <typename T, int D, bool CAUSAL, int NW>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
@@ -820,23 +819,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     // Two 32-key halves, so that only one half's S and dP are live at a time.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // S^T and dP^T alternate (K and V fragments of one contraction step),
-      // each fragment read kDqAhead products before its use so that the LDS
-      // latency passes behind the products in between.
       f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        constexpr int NP = 2 * KS, R = kDqAhead + 1;
-        F fr[R];
-        auto rd = [&](int y) { rf.read(fr[y % R], (y & 1) ? sV : sK, kb, y >> 1); };
 #pragma unroll
-        for (int y = 0; y < kDqAhead; ++y) rd(y);
-#pragma unroll
-        for (int y = 0; y < NP; ++y) {
-          if (y + kDqAhead < NP) rd(y + kDqAhead);
-          if (y & 1) dp = mfma_k16(fr[y % R], of[y >> 1], dp);
-          else s = mfma_k16(fr[y % R], qf[y >> 1], s);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        F kf, vf;
+        rf.read(kf, sK, kb, ks);
+        rf.read(vf, sV, kb, ks);
+        s = mfma_k16(kf, qf[ks], s);
+        dp = mfma_k16(vf, of[ks], dp);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
