@@ -55,7 +55,6 @@ constexpr int kWavesBf16 = 8;
 constexpr int kWavesF32 = 4;
 constexpr int kBc = 64;           // keys per tile
 constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
-constexpr int kAhead = 4;         // K fragments read ahead of their score product
 // bf16: a tile is first exponentiated against the running max as it stands;
 // the result is kept when every lane's share of the tile's row sum is at most
 // this (so every p <= 2^15, inside fp16 range).  Otherwise the tile max is
@@ -150,22 +149,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   auto tile = [&](const char* sK, const char* sV, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (MASK && CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
-    // Scores: the 2 KS products alternate between the two 32-key blocks, and
-    // each K fragment is read kAhead products before its use, so that the
-    // LDS latency passes behind the products in between (read just before
-    // its product, every fragment would stall the wave on its own read).
     f32x16 s[2];
-    s[0] = s[1] = f32x16{};
-    {
-      constexpr int NP = 2 * KS, R = kAhead + 1;
-      F kr[R];
 #pragma unroll
-      for (int y = 0; y < kAhead; ++y) rf.read(kr[y], sK, y & 1, y >> 1);
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-      for (int y = 0; y < NP; ++y) {
-        if (y + kAhead < NP) rf.read(kr[(y + kAhead) % R], sK, (y + kAhead) & 1, (y + kAhead) >> 1);
-        s[y & 1] = mfma_k16(kr[y % R], qf[y >> 1], s[y & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) {
+        F kf;
+        rf.read(kf, sK, kb, ks);
+        s[kb] = mfma_k16(kf, qf[ks], s[kb]);
       }
     }
     if (MASK) {
