@@ -101,6 +101,17 @@ def test_decode_workloads_full(name):
     _check(w, inp, o, lse)
 
 
+def test_decode_long_cache_peaked_rows():
+    # The long-sequence distribution (Q and K with std 2: logits with std 4,
+    # peaked rows) against a 65536-token cache, held to the flat O bar of the
+    # named bf16 workloads (1e-2 max abs) besides the bf16 rounding bound.
+    w = synth.KvWorkload("decode_long_std2", 1, 8, 8, 1, 65536, 128, "bf16", True, seed=7300, qk_std=2.0)
+    inp, o, lse = _run(w, 0)
+    _check(w, inp, o, lse)
+    O, _ = attention_fwd_kv_ref(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.scale, True)
+    assert float(np.max(np.abs(o - O))) <= 1e-2
+
+
 @pytest.mark.parametrize("dt,d", [("f32", 64), ("bf16", 128)])
 def test_merge_of_oracle_ranges(dt, d):
     import torch

@@ -136,6 +136,7 @@ class KvWorkload:
     dtype: str
     causal: bool
     seed: int = 0
+    qk_std: float = 1.0
 
     @property
     def scale(self) -> float:
@@ -154,12 +155,13 @@ KV_WORKLOADS = {
 
 
 def make_kv_inputs(w: KvWorkload, seed: int | None = None) -> Inputs:
-    """Seeded q [B,H,Nq,d], k and v [B,Hkv,Nk,d], iid N(0,1), drawn in that
-    order like make_inputs; bf16 workloads are rounded to bf16 (RNE)."""
+    """Seeded q [B,H,Nq,d], k and v [B,Hkv,Nk,d], drawn in that order like
+    make_inputs: q and k iid N(0, qk_std^2), v iid N(0, 1); bf16 workloads are
+    rounded to bf16 (RNE)."""
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     raw = {
-        "q": rng.standard_normal((w.B, w.H, w.Nq, w.d), dtype=np.float32),
-        "k": rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32),
+        "q": rng.standard_normal((w.B, w.H, w.Nq, w.d), dtype=np.float32) * np.float32(w.qk_std),
+        "k": rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32) * np.float32(w.qk_std),
         "v": rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32),
     }
     if w.dtype == "f32":
