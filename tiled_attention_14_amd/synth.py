@@ -171,3 +171,65 @@ def make_kv_inputs(w: KvWorkload, seed: int | None = None) -> Inputs:
     bits = {n: bf16_round_bits(a) for n, a in raw.items()}
     vals = {n: bf16_bits_to_f32(b) for n, b in bits.items()}
     return Inputs(w, vals, bits)
+
+
+# ---------------------------------------------------------------- fp8 (OCP e4m3) inputs
+# 8-bit floats in the OCP "E4M3" format: sign, 4 exponent bits (bias 7), 3
+# mantissa bits; exponent field 0 holds subnormals (m / 8 * 2^-6); the code
+# S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448;
+# there is no infinity.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 e4m3 codes -> float64 values (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float -> nearest e4m3 code (ties to even), saturating at +-448.  Finite inputs only."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("e4m3_encode expects finite values")
+    table = e4m3_decode(np.arange(128, dtype=np.uint8))   # non-negative codes 0..127
+    finite = np.arange(127)                               # 127 is NaN
+    vals = table[finite]
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(vals, a, side="left").clip(0, 126)
+    lo = (hi - 1).clip(0, 126)
+    dlo, dhi = np.abs(a - vals[lo]), np.abs(vals[hi] - a)
+    # nearest; on a tie the even code (its mantissa's last bit 0)
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(x < 0, 0x80, 0)).astype(np.uint8)
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    """fp8 attention inputs: e4m3 codes and per-tensor scales; ``f64(name)`` is
+    the value the library computes with (decoded code times scale)."""
+    codes: dict
+    scales: dict
+
+    def f64(self, name: str) -> np.ndarray:
+        return e4m3_decode(self.codes[name]) * self.scales[name]
+
+
+def make_fp8_inputs(B, H, Hkv, N, d, seed, qk_std=1.0) -> Fp8Inputs:
+    """Seeded Q, K, V (iid normal, drawn in that order) quantized per tensor to
+    e4m3 with the scale that maps the tensor's largest magnitude to 448."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    raw = {"q": rng.standard_normal((B, H, N, d), dtype=np.float32) * np.float32(qk_std),
+           "k": rng.standard_normal((B, Hkv, N, d), dtype=np.float32) * np.float32(qk_std),
+           "v": rng.standard_normal((B, Hkv, N, d), dtype=np.float32)}
+    codes, scales = {}, {}
+    for n, a in raw.items():
+        s = float(np.float32(np.max(np.abs(a)) / E4M3_MAX))
+        codes[n] = e4m3_encode(a / s)
+        scales[n] = s
+    return Fp8Inputs(codes, scales)
