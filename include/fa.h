@@ -78,6 +78,25 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    float scale, int causal, fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Forward pass on 8-bit float inputs.  q, k, v hold OCP e4m3 codes (one byte
+ * per element: sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * finite 448) in the layouts above; the value of an element is its code
+ * times the tensor's scale (q_scale, k_scale, v_scale: finite, > 0).  Writes
+ * o in bf16 and lse as fa_fwd does, for o = softmax(scale * Q K^T) V of those
+ * values.  Both products run on the 8-bit matrix cores with float32
+ * accumulation; the probabilities are rounded to e4m3 for the P V product
+ * (relative error at most 2^-4 each), while the row sums and lse use them
+ * unrounded.  The fp8 variant of the pages' kernel family ("【词汇专栏】
+ * FlashAttention", section 3.3, FA3) fixes no scaling recipe; this is
+ * per-tensor scaling.  d must be 128 (FA_ERR_UNSUPPORTED otherwise).
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v,
+                       void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d,
+                       float scale, float q_scale, float k_scale, float v_scale,
+                       int causal, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: two float32 per
  * query row (-D_i = -sum_c dO_ic * O_ic and lse_i * log2 e) and, only for GQA
  * shapes whose query heads are spread over several workgroups of the dK/dV

@@ -30,7 +30,8 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess", "fa_bwd_workspace_size",
-                     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge", "fa_status_string"]
+                     "fa_fwd", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge",
+                     "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -231,3 +232,30 @@ def test_merge_invalid_arguments(lib, args, status):
     a = dict(nsplit=3, rows=10, d=64, dtype=fa.FA_F32, ptrs=[P] * 4)
     a.update(args)
     assert fa.fa_merge(*a["ptrs"], a["nsplit"], a["rows"], a["d"], a["dtype"], 0) == status
+
+
+# ------------------------------------------------------------------ fp8 forward
+F8 = dict(B=1, H=4, Hkv=2, N=100, d=128, scale=0.09, qs=0.01, ks=0.01, vs=0.01, causal=1)
+
+
+def _fp8(**kw):
+    a = dict(F8); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 5)
+    return fa.fa_fwd_fp8(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["qs"], a["ks"], a["vs"],
+                         a["causal"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(qs=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(ks=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(ptrs=[P, None, P, P, P]), fa.FA_ERR_INVALID_ARG),
+    (dict(ptrs=[P, P, P, P, P + 4]), fa.FA_ERR_INVALID_ARG),
+])
+def test_fp8_invalid_arguments(lib, kw, status):
+    assert _fp8(**kw) == status

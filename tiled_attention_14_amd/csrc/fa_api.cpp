@@ -154,6 +154,24 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return fa::launch_fwd(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int N, int d, float scale, float q_scale, float k_scale, float v_scale, int causal,
+                       hipStream_t stream) {
+  if (!all_aligned({q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
+  for (float x : {q_scale, k_scale, v_scale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  // Shape rules of the bf16 path (a one-byte slab is half a bf16 one).
+  fa_status_t st = check_shape(B, H, Hkv, N, 128, FA_BF16, scale);
+  if (st != FA_OK) return st;
+  fa::Fp8Params p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.N = N;
+  p.scale = scale; p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.causal = causal != 0;
+  return fa::launch_fwd_fp8(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, fa_dtype_t dtype) {
   if (check_shape(B, H, Hkv, N, d, dtype, 1.0f) != FA_OK) return 0;
   const int ns = std::max(dkdv_nsplit(B, H, Hkv, N, false, dtype), dkdv_nsplit(B, H, Hkv, N, true, dtype));

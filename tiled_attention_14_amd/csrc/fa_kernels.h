@@ -60,7 +60,17 @@ struct MergeParams {
   Dtype dtype;
 };
 
+// Forward on OCP e4m3 codes (d = 128): element value = code * tensor scale.
+struct Fp8Params {
+  const void* q; const void* k; const void* v;
+  void* o; float* lse;
+  int B, H, Hkv, N;
+  float scale, q_scale, k_scale, v_scale;
+  bool causal;
+};
+
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 hipError_t launch_fwd_split(const SplitParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 // Backward phases, in stream order: preprocess (D and lse2), then the dK/dV

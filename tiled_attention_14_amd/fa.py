@@ -1,6 +1,6 @@
 """Thin Python binding of the C ABI in ``include/fa.h``.
 
-``fa_fwd``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_fwd_splitkv``,
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_merge``,
 ``fa_bwd_dq``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
 the C names and argument order; pointer arguments accept an integer device
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_splitkv.restype = I
         L.fa_merge.argtypes = [P, P, P, P, I, ctypes.c_long, I, I, P]
         L.fa_merge.restype = I
+        L.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, P]
+        L.fa_fwd_fp8.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -113,6 +115,11 @@ def fa_bwd_dq(q, k, v, dO, dq, B, H, Hkv, N, d, scale, causal, dtype,
     return lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq),
                            B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
                            _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, N, d, scale, q_scale, k_scale, v_scale, causal, stream=None) -> int:
+    return lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
+                            float(q_scale), float(k_scale), float(v_scale), int(bool(causal)), _stream(stream))
 
 
 def fa_fwd_splitkv_workspace_size(B, H, Hkv, Nq, Nk, d, dtype, nsplit=0) -> int:
