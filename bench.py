@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix and vector)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SOURCES = {"fa_fwd": ["tiled_attention_14_amd/csrc/fa_fwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"],
                   "fa_bwd_dkdv": ["tiled_attention_14_amd/csrc/fa_bwd.hip", "tiled_attention_14_amd/csrc/fa_device.h"],
@@ -145,6 +146,43 @@ def decode_leg(dev, calls=50, warmup=10):
     return res
 
 
+def fp8_leg(dev, calls=50, warmup=10):
+    """Times fa_fwd_fp8 on the headline shape (e4m3 Q, K, V with per-tensor
+    scales, bf16 O) with HIP events on the launch stream; the rate is the
+    forward's algorithmic flops against the dense fp8 matrix-core peak."""
+    import numpy as np
+    import torch
+    from tiled_attention_14_amd import fa, synth
+    w = synth.WORKLOADS[synth.HEADLINE]
+    inp = synth.make_fp8_inputs(w.B, w.H, w.Hkv, w.N, w.d, seed=w.seed)
+    t = {n: torch.from_numpy(inp.codes[n]).to(dev) for n in ("q", "k", "v")}
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        st = fa.fa_fwd_fp8(t["q"], t["k"], t["v"], o, lse, w.B, w.H, w.Hkv, w.N, w.d, w.scale,
+                           inp.scales["q"], inp.scales["k"], inp.scales["v"], w.causal, stream)
+        if st != fa.FA_OK:
+            raise RuntimeError("fa_fwd_fp8 failed")
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    f_fwd = flops(w)[0]
+    tf = f_fwd / (ms * 1e-3) / 1e12
+    log(f"[bench] fp8 forward {w.name}: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+    return {"workload": w.name, "dtype": "e4m3 in, bf16 out", "ms": round(ms, 4), "tflops": round(tf, 2),
+            "bound": "mfma", "peak": PEAK_FP8_TFLOPS, "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+
 def main():
     from tiled_attention_14_amd import synth
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -153,7 +191,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-decode", action="store_true", help="skip the key/value-cache decode leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode and fp8 legs (headline only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -283,6 +321,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }
     out["decode"] = None if args.no_decode else decode_leg(dev)
+    out["fp8_forward"] = None if args.no_decode else fp8_leg(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
