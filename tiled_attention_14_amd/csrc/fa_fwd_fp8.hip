@@ -14,11 +14,14 @@
 //    lazy running max, so 2^7 P stays below the format's 448); the row sum
 //    and the log-sum-exp take the fp32 P, so only the P V product sees the
 //    rounding (relative error at most 2^-4 per probability);
-//  * O^T += V^T P^T: a 32-byte operand fragment holds the 32 keys that the
-//    lane's P registers hold, in the order of those registers.  V is written
-//    to its LDS tile transposed (one row per column of V) with its keys in
-//    that order, so the fragment is two 16-byte reads.  The tile is filled
-//    from registers, one byte per store.
+//  * O^T += V^T P^T: a 32-byte operand fragment holds one column of V over
+//    the 32 keys that the lane's P registers hold, in the order of those
+//    registers.  V tiles are copied global -> LDS like K tiles (row-major),
+//    and the gfx950 transposing read ds_read_b64_tr_b8 gathers the column:
+//    within each 16-lane group, byte e of result lane j is byte j % 8 of the
+//    8 bytes that lane 2 e + j / 8 addresses, so source lanes 2 e and 2 e + 1
+//    address the same key row at columns C and C + 8, and four reads (keys
+//    16 apart) give the 32 keys.
 //
 // d = 128 only.  O is written in bf16, LSE in fp32, as for fa_fwd.
 #include "fa_device.h"
@@ -30,12 +33,12 @@ namespace fa {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kW8 = 8;              // waves (32 query rows each)
 constexpr int kBr8 = 32 * kW8;      // query rows per workgroup
 constexpr int kBc8 = 64;            // keys per tile
 constexpr int kD8 = 128;            // head size (bytes per row of Q, K, V)
-constexpr int kVtRow = 80;          // bytes per row of the transposed V tile: 64 keys + 16 of padding
 constexpr float kSlack8 = 1.f;      // log2 units the running max may lag behind
 constexpr float kPExp = 7.f;        // P is stored as e4m3(2^kPExp p)
 
@@ -55,21 +58,11 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
 // elements, so the bf16 d = 64 tile layout, copy and row-fragment reads serve.
 typedef Lay<bf16, 64> KL;
 
-// Position of key `key` (0..63 of a tile) inside its row of the transposed V
-// tile: lane half hf = (key % 8) / 4 reads positions 32 hf .. 32 hf + 31, in the
-// order of the P registers (block key / 32, then register 4 j + e of that block).
-__device__ __forceinline__ int vt_pos(int key) {
-  const int kb = key >> 5, j = (key >> 3) & 3, hf = (key >> 2) & 1, e = key & 3;
-  return 32 * hf + 16 * kb + 4 * j + e;
-}
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
-  constexpr int TBK = kBc8 * KL::RB;        // 8 KB K tile
-  constexpr int TBV = kD8 * kVtRow;         // 10 KB transposed V tile
+  constexpr int TBK = kBc8 * KL::RB;        // 8 KB K or V tile
   constexpr int DB = kD8 / 32;
-  __shared__ __attribute__((aligned(1024))) char sK0[TBK], sK1[TBK];
-  __shared__ __attribute__((aligned(1024))) char sV0[TBV], sV1[TBV];
+  __shared__ __attribute__((aligned(1024))) char sK0[TBK], sK1[TBK], sV0[TBK], sV1[TBK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,27 +99,29 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   TileCopy<bf16, 64, kBc8, kW8> tc;
   rf.init();
   tc.init(w);
-  // V: thread t moves 16 bytes, key t / 8, columns 16 (t % 8) .. + 15.
-  const int vkey = tid >> 3, vcol = (tid & 7) * 16;
-  const int vpos = vt_pos(vkey);
-  u32x4 vr;
-  auto load_v = [&](int k0) {
-    const rsrc_t rs = make_rsrc(Vh + (size_t)k0 * kD8, (uint32_t)(N - k0) * (uint32_t)kD8);
-    vr = load16(rs, (uint32_t)(vkey * kD8 + vcol));
-  };
-  auto store_v = [&](char* sV) {
+  // Transposing reads of V: source lane 16 G + s addresses key row
+  // 8 (e / 4) + 4 hf + e % 4 (+ 16 r for read r), e = s / 2, at columns
+  // 32 db + 16 (G % 2) + 8 (s % 2) .. + 7; result lane l then holds column
+  // 32 db + l % 32 over the keys of P register slots 8 r .. 8 r + 7.  The
+  // tile's granule permutation depends on row bits 1-3 only, so read r is an
+  // immediate offset of 16 r rows.
+  int voff[DB];
+  {
+    const int s16 = lane & 15, e = s16 >> 1;
+    const int vkey = 8 * (e >> 2) + 4 * hf + (e & 3);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      sV[(vcol + e) * kVtRow + vpos] = (char)((vr[e >> 2] >> (8 * (e & 3))) & 0xff);
+    for (int db = 0; db < DB; ++db) voff[db] = KL::off(vkey, (32 * db + 16 * ((lane >> 4) & 1) + 8 * (s16 & 1)) / 2);
+  }
+  auto copy_kv = [&](char* sK, char* sV, int k0) {
+    tc.issue(reinterpret_cast<const bf16*>(Kh), N, k0, sK);
+    tc.issue(reinterpret_cast<const bf16*>(Vh), N, k0, sV);
   };
 
   lds_zero<64 * kW8>(sK0, TBK); lds_zero<64 * kW8>(sK1, TBK);
-  lds_zero<64 * kW8>(sV0, TBV); lds_zero<64 * kW8>(sV1, TBV);
+  lds_zero<64 * kW8>(sV0, TBK); lds_zero<64 * kW8>(sV1, TBK);
   __syncthreads();
-  tc.issue(reinterpret_cast<const bf16*>(Kh), N, 0, sK0);
-  load_v(0);
+  copy_kv(sK0, sV0, 0);
   wait_copies();
-  store_v(sV0);
   __syncthreads();
 
   float m = -INFINITY, lsum = 0.f;
@@ -191,12 +186,14 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
       }
     lsum += ts;
     // O^T += V^T P^T: one 64-deep product per 32 columns of V.
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const char* row = sV + (32 * db + l32) * kVtRow + 32 * hf;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(row);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 16);
-      const i32x8 vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      i32x2 c[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        c[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)((lds_void*)(sV + voff[db] + 16 * r * KL::RB)));
+      const i32x8 vf = {c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
       acc[db] = mfma8(vf, pf, acc[db]);
     }
   };
@@ -205,13 +202,9 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
 
   const int jfull = min(nt, CAUSAL ? (qt * kBr8) / kBc8 : N / kBc8);
   auto step = [&](int j, char* sKc, char* sVc, char* sKn, char* sVn, auto mask_tag) {
-    if (j + 1 < nt) {
-      tc.issue(reinterpret_cast<const bf16*>(Kh), N, (j + 1) * kBc8, sKn);
-      load_v((j + 1) * kBc8);
-    }
+    if (j + 1 < nt) copy_kv(sKn, sVn, (j + 1) * kBc8);
     tile(sKc, sVc, j * kBc8, mask_tag);
     wait_copies();
-    if (j + 1 < nt) store_v(sVn);
     __syncthreads();
   };
   int j = 0;
