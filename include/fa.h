@@ -155,6 +155,48 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Attention with dropout on the probabilities, fused into the forward and
+ * backward passes ("FlashAttention 在昇腾NPU上到底快在哪", section 二, names
+ * dropout fused into the attention operator together with the softmax; the
+ * rate argument is that of PyTorch's fused attention in "【词汇专栏】FlashAttention",
+ * section 5.1).  The pages give neither the generator nor the keep rule; this
+ * library defines them:
+ *
+ *     P = softmax(scale * Q K^T) (masks as in fa_fwd),  O = (P * M / keep) V
+ *     lse: as in fa_fwd (the mask M does not enter it)
+ *
+ * M[b,h,i,j] is 1 when the byte of element (i, j) is >= t, t = round(256 * p_drop),
+ * keep = (256 - t) / 256.  The bytes come from Philox4x32-10 (Salmon et al.,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011): one call per 4 x 4
+ * block of query rows 4a..4a+3 and keys 4c..4c+3, with counter
+ * (c, a, b*H + h, offset) and key (seed & 0xffffffff, seed >> 32); word r of
+ * the result belongs to query 4a + r, its byte e (little-endian) to key 4c + e.
+ * The mask depends on (seed, offset, b, h, i, j) only, so fa_bwd_dropout with
+ * the same seed and offset regenerates it instead of reading it, and a caller
+ * that varies `offset` per call (or per layer) gets fresh masks.
+ *
+ * p_drop: finite, 0 <= p_drop with round(256 * p_drop) <= 255 (the rate is
+ * quantised to t/256); t == 0 runs fa_fwd / fa_bwd.  Otherwise the same
+ * arguments, layouts, workspace, ownership and errors as fa_fwd and fa_bwd.
+ * fa_bwd_dropout takes the O written by fa_fwd_dropout and returns the
+ * gradients of sum(O * dO) for that same mask.
+ */
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int N, int d,
+                           float scale, int causal, float p_drop,
+                           unsigned long long seed, unsigned int offset,
+                           fa_dtype_t dtype, hipStream_t stream);
+
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int B, int H, int Hkv, int N, int d,
+                           float scale, int causal, float p_drop,
+                           unsigned long long seed, unsigned int offset,
+                           fa_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Attention over a key/value cache: Nq query rows against Nk keys.
  *
  *   q, o : [B, H, Nq, d]    k, v : [B, Hkv, Nk, d]    lse : [B, H, Nq] float32

@@ -29,8 +29,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_preprocess", "fa_bwd_workspace_size",
-                     "fa_fwd", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge",
+    assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout", "fa_bwd_preprocess",
+                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge",
                      "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
@@ -259,3 +259,44 @@ def _fp8(**kw):
 ])
 def test_fp8_invalid_arguments(lib, kw, status):
     assert _fp8(**kw) == status
+
+
+def _fwd_drop(p_drop, **kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 5)
+    return fa.fa_fwd_dropout(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], p_drop,
+                             0x1234, 7, a["dtype"], 0)
+
+
+def _bwd_drop(p_drop, **kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 9)
+    ws = a.pop("ws", P)
+    return fa.fa_bwd_dropout(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], p_drop,
+                             0x1234, 7, a["dtype"], ws, 1 << 40, 0)
+
+
+@pytest.mark.parametrize("p_drop", [-0.01, float("nan"), float("inf"), 0.999, 1.0, 2.0])
+def test_dropout_rate_rejected(lib, p_drop):
+    assert _fwd_drop(p_drop) == fa.FA_ERR_INVALID_ARG
+    assert _bwd_drop(p_drop) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("p_drop", [0.0, 0.1, 255 / 256])
+@pytest.mark.parametrize("kw,status", [(dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(H=3), fa.FA_ERR_INVALID_ARG),
+                                       (dict(N=0), fa.FA_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+                                       (dict(dtype=5), fa.FA_ERR_UNSUPPORTED)])
+def test_dropout_shape_errors(lib, p_drop, kw, status):
+    # Valid rates (0 included, which takes the plain entry points) with a bad shape.
+    assert _fwd_drop(p_drop, **kw) == status
+    assert _bwd_drop(p_drop, **kw) == status
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_dropout_null_and_misaligned_pointers(lib, i):
+    for bad in (0, P + 4):
+        ptrs = [P] * 5; ptrs[i] = bad
+        assert _fwd_drop(0.2, ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+        ptrs = [P] * 9; ptrs[i] = bad
+        assert _bwd_drop(0.2, ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+    assert _bwd_drop(0.2, ws=0) == fa.FA_ERR_WORKSPACE

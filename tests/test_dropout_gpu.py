@@ -1,0 +1,110 @@
+"""Parity of the dropout entry points (``fa_fwd_dropout`` and ``fa_bwd_dropout``,
+through the C ABI) with the float64 dropout oracle of ``oracle/dropout.py``.
+
+* The mask itself, bit for bit: with V = I (rows of the identity, d >= N), O's
+  zero pattern is the keep mask on the visible scores; with dO = I, dV's zero
+  pattern is its transpose.  This checks the generator, the 4 x 4 block map
+  and the threshold in the forward and in the dK/dV kernel as integer work.
+* A sweep of shapes over several tiles with ragged ends, both dtypes, both
+  head sizes, GQA and MHA, causal and not, several rates, seeds and offsets,
+  compared element by element on O, LSE, dQ, dK, dV with the bars of the
+  square-attention tests (f32: 1e-5 * max(1, max |ref|); bf16: LSE 1e-3, O
+  within max(1e-2, 1.05 u (attn(|V|) + |O|) + 1e-5), u = 2^-8, attn(|V|)
+  being the oracle's dropout attention of |V|; dQ/dK/dV relative L2 2e-2).
+* Rate 0 runs the plain path; LSE does not depend on the mask.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention_fwd_ref
+from oracle.dropout import attention_bwd_dropout_ref, attention_fwd_dropout_ref, keep_mask
+from tiled_attention_14_amd import fa, synth
+
+from gpu_common import check, host64, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, p, seed, offset, t=None):
+    import torch
+    inp = synth.make_inputs(w)
+    t = to_device(inp) if t is None else t
+    say(f"[dropout] {w.name} B={w.B} H={w.H} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} causal={w.causal} "
+        f"p={p} seed={seed:#x} offset={offset}")
+    o, lse = fa.forward_dropout(t["q"], t["k"], t["v"], p, seed, offset, w.scale, w.causal)
+    dq, dk, dv = fa.backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, p, seed, offset, w.scale, w.causal)
+    torch.cuda.synchronize()
+    return inp, {n: host64(x) for n, x in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+
+
+def _refs(w, inp, p, seed, offset):
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    O, L = attention_fwd_dropout_ref(q, k, v, w.scale, w.causal, p, seed, offset)
+    dq, dk, dv = attention_bwd_dropout_ref(q, k, v, do, w.scale, w.causal, p, seed, offset)
+    floor = None
+    if w.dtype == "bf16":
+        floor, _ = attention_fwd_dropout_ref(q, k, np.abs(v), w.scale, w.causal, p, seed, offset)
+    return {"o": O, "lse": L, "dq": dq, "dk": dk, "dv": dv}, floor
+
+
+@pytest.mark.parametrize("dt,d,N,causal", [("bf16", 128, 128, False), ("bf16", 64, 61, True),
+                                           ("f32", 128, 100, True), ("f32", 64, 64, False)])
+def test_mask_bit_exact(dt, d, N, causal):
+    import torch
+    B, H, p, seed, off = 2, 3, 0.3, 0xDEADBEEF12345, 11
+    w = synth.Workload("mask_exact", B, H, H, N, d, dt, causal, seed=9000 + N + d)
+    inp = synth.make_inputs(w)
+    t = to_device(inp)
+    eye = torch.zeros((B, H, N, d), dtype=t["v"].dtype, device="cuda")
+    idx = torch.arange(N, device="cuda")
+    eye[:, :, idx, idx] = 1
+    t["v"] = eye.contiguous()
+    t["do"] = eye.clone()
+    _, got = _run(w, p, seed, off, t)
+    M, _ = keep_mask(B, H, N, N, p, seed, off)
+    vis = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    want = (M > 0) & vis
+    o_nz = got["o"][..., :N] != 0
+    dv_nz = np.swapaxes(got["dv"][..., :N], -1, -2) != 0   # dV[j, i] = Z[i, j]
+    say(f"[dropout]   kept {want.mean():.3f}; O pattern mismatches {int((o_nz != want).sum())}, "
+        f"dV pattern mismatches {int((dv_nz != want).sum())}")
+    assert np.array_equal(o_nz, want)
+    assert np.array_equal(dv_nz, want)
+    assert not np.any(got["o"][..., N:])
+
+
+SWEEP = [
+    # dtype, d, causal, B, H, Hkv, N, p, seed, offset
+    ("bf16", 128, True, 1, 4, 2, 300, 0.1, 1, 0),
+    ("bf16", 128, False, 2, 2, 1, 129, 0.5, 2 ** 40 + 3, 9),
+    ("bf16", 64, True, 1, 8, 1, 777, 0.2, 77, 1),
+    ("bf16", 64, False, 1, 4, 4, 1000, 0.3, 5, 2 ** 32 - 1),
+    ("bf16", 128, True, 1, 2, 2, 1, 0.5, 6, 0),     # 1/keep = 2: O = 2 V exactly, so dS = 0 stays ~0
+    ("f32", 128, True, 1, 4, 2, 300, 0.25, 7, 3),
+    ("f32", 64, False, 2, 3, 3, 200, 0.6, 8, 4),
+    ("f32", 64, True, 1, 2, 1, 65, 0.9, 9, 5),
+]
+
+
+@pytest.mark.parametrize("dt,d,causal,B,H,Hkv,N,p,seed,offset", SWEEP, ids=lambda x: str(x))
+def test_dropout_sweep(dt, d, causal, B, H, Hkv, N, p, seed, offset):
+    w = synth.Workload("dropout_sweep", B, H, Hkv, N, d, dt, causal, seed=9100 + N + d + H + causal)
+    inp, got = _run(w, p, seed, offset)
+    ref, floor = _refs(w, inp, p, seed, offset)
+    check(w, got, ref, "dropout", f32_scaled=True, o_floor=floor)
+
+
+def test_rate_zero_is_the_plain_path_and_lse_ignores_the_mask():
+    import torch
+    w = synth.Workload("dropout_zero", 1, 4, 2, 257, 128, "bf16", True, seed=9200)
+    inp = synth.make_inputs(w)
+    t = to_device(inp)
+    o0, l0 = fa.forward(t["q"], t["k"], t["v"], w.scale, True)
+    o1, l1 = fa.forward_dropout(t["q"], t["k"], t["v"], 0.0, 123, 0, w.scale, True)
+    o2, l2 = fa.forward_dropout(t["q"], t["k"], t["v"], 0.5, 123, 0, w.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert float((l0 - l2).abs().max()) <= 1e-6
+    assert not torch.equal(o0, o2)
+    _, L = attention_fwd_ref(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.scale, True)
+    assert float(np.max(np.abs(host64(l2) - L))) <= 1e-3

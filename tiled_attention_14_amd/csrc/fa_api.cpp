@@ -131,6 +131,21 @@ size_t splitkv_bytes(int B, int H, int Nq, int d, int count, size_t* lse_off) {
   return *lse_off + round_up(rows * sizeof(float), kAlign);
 }
 
+// Byte threshold t = round(256 p_drop) (1..255 turns dropout on; 0 leaves it off)
+// and the inverted-dropout scale 256 / (256 - t).
+bool drop_params(float p_drop, unsigned long long seed, unsigned int offset, fa::DropParams* out) {
+  if (!std::isfinite(p_drop) || p_drop < 0.f) return false;
+  const double t = std::floor(256.0 * (double)p_drop + 0.5);
+  if (t > 255.0) return false;
+  out->on = t > 0.0;
+  out->t = (uint32_t)t;
+  out->k0 = (uint32_t)(seed & 0xffffffffull);
+  out->k1 = (uint32_t)(seed >> 32);
+  out->offset = offset;
+  out->inv = (float)(256.0 / (256.0 - t));
+  return true;
+}
+
 bool all_aligned(std::initializer_list<const void*> ps) {
   for (const void* x : ps)
     if (!x || !aligned16(x)) return false;
@@ -218,6 +233,45 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
+  if (fa::launch_bwd_pre(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                           int N, int d, float scale, int causal, float p_drop, unsigned long long seed,
+                           unsigned int offset, fa_dtype_t dtype, hipStream_t stream) {
+  fa::DropParams dp;
+  if (!drop_params(p_drop, seed, offset, &dp)) return FA_ERR_INVALID_ARG;
+  if (!dp.on) return fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dtype, stream);
+  if (!all_aligned({q, k, v, o, lse})) return FA_ERR_INVALID_ARG;
+  fa_status_t st = check_shape(B, H, Hkv, N, d, dtype, scale);
+  if (st != FA_OK) return st;
+  fa::FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Hkv = Hkv; p.N = N; p.d = d;
+  p.scale = scale; p.causal = causal != 0;
+  p.dtype = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
+  p.drop = dp;
+  return fa::launch_fwd(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                           float scale, int causal, float p_drop, unsigned long long seed, unsigned int offset,
+                           fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::DropParams dp;
+  if (!drop_params(p_drop, seed, offset, &dp)) return FA_ERR_INVALID_ARG;
+  if (!dp.on)
+    return fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, workspace,
+                  workspace_bytes, stream);
+  if (!all_aligned({q, k, v, o, dO, lse, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  fa::BwdParams p;
+  fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
+  if (st != FA_OK) return st;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
+  p.drop = dp;
   if (fa::launch_bwd_pre(p, stream) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;

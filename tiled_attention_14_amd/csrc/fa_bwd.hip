@@ -54,6 +54,7 @@ struct BwdArgs {
   int B, H, Hkv, N, nsplit;
   float c;      // scale * log2(e)
   float scale;
+  DropArgs drop;
 };
 
 BwdArgs make_args(const BwdParams& p) {
@@ -64,6 +65,7 @@ BwdArgs make_args(const BwdParams& p) {
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N; a.nsplit = p.nsplit;
   a.c = p.scale * kLog2e;
   a.scale = p.scale;
+  a.drop = DropArgs{p.drop.k0, p.drop.k1, p.drop.offset, p.drop.t, p.drop.inv};
   return a;
 }
 
@@ -106,7 +108,7 @@ constexpr int kKeys = kDkdvKeysF32;    // keys per workgroup (32 per wave)
 constexpr int kQRows = kDkdvQRowsF32;  // query rows per step
 static_assert(kKeys == 32 * kWaves, "one 32-key column block per wave");
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   typedef typename Frag<T>::type F;
   typedef Lay<T, D> L;
@@ -193,6 +195,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int qb0 = (qstart + it % nq) * kQRows;
     if (MASK && CAUSAL && qb0 + kQRows - 1 < kw) return;  // every query of the step is before every key of the wave
+    const uint32_t bhq = (uint32_t)(b * a.H + h0 + it / nq);
     f32x16 s[MB], dp[MB];
     auto sdp = [&](int mb) {
       s[mb] = f32x16{};
@@ -215,6 +218,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         const int ql0 = mb * 32 + 8 * g4 + 4 * hf;
         const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql0);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(sD + ql0);
+        // Dropout: the generator's block of queries qb0 + ql0 + 0..3 and this
+        // lane's key; word e belongs to query e, byte mykey % 4 to the key.
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (DROP) x = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qb0 + ql0) >> 2, bhq, a.drop.offset,
+                                              a.drop.k0, a.drop.k1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
@@ -223,8 +231,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             const int c = mb * 32 + 8 * g4 + e;  // ql - 4 hf
             if ((CAUSAL && c < lim) || c > qlim) p = 0.f;
           }
-          s[mb][i] = p;
-          dp[mb][i] = p * (dp[mb][i] + dd[e]);
+          if constexpr (DROP) {
+            const bool keep = drop_keep(x[e], 8u * (mykey & 3), a.drop.t);
+            s[mb][i] = keep ? p : 0.f;
+            dp[mb][i] = p * __builtin_fmaf(dp[mb][i], keep ? a.drop.inv : 0.f, dd[e]);
+          } else {
+            s[mb][i] = p;
+            dp[mb][i] = p * (dp[mb][i] + dd[e]);
+          }
         }
       }
     };
@@ -334,6 +348,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   typedef std::integral_constant<bool, true> Any;
   auto run = [&](const char* sQ, const char* sO, const float* sL, const float* sD, int it) {
     if (masked(it)) step(sQ, sO, sL, sD, it, Any());
+    else if constexpr (DROP) step(sQ, sO, sL, sD, it, Full());
     else step_full(sQ, sO, sL, sD);
   };
 
@@ -354,16 +369,18 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
 
   if (a.nsplit == 1) {
     store_rows<T, D>(reinterpret_cast<T*>(a.dk) + (size_t)bkv * slab, mykey, N, dk, a.scale);
-    store_rows<T, D>(reinterpret_cast<T*>(a.dv) + (size_t)bkv * slab, mykey, N, dv, 1.f);
+    store_rows<T, D>(reinterpret_cast<T*>(a.dv) + (size_t)bkv * slab, mykey, N, dv, DROP ? a.drop.inv : 1.f);
   } else {
     const size_t ps = (size_t)a.B * a.Hkv * slab;  // elements of one partial tensor
     store_rows<float, D>(a.part + (2 * sp) * ps + (size_t)bkv * slab, mykey, N, dk, a.scale);
-    store_rows<float, D>(a.part + (2 * sp + 1) * ps + (size_t)bkv * slab, mykey, N, dv, 1.f);
+    store_rows<float, D>(a.part + (2 * sp + 1) * ps + (size_t)bkv * slab, mykey, N, dv, DROP ? a.drop.inv : 1.f);
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_f32(BwdArgs a) { dkdv_body<float, D, CAUSAL>(a); }
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel_f32(BwdArgs a) {
+  dkdv_body<float, D, CAUSAL, DROP>(a);
+}
 
 // ------------------------------------------------------------------ 2b. dK / dV, bf16: wave pairs
 // Eight waves and 256 keys per workgroup; the four wave pairs own 64 keys
@@ -387,7 +404,7 @@ constexpr int kPairRows = kDkdvQRowsBf16;
 static_assert(kPairKeys == 64 * (kPairWaves / 2) && kPairRows == 32, "64 keys per pair, 32-row steps");
 constexpr int kPairAhead = 2;  // fragment reads in flight ahead of their products
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   typedef bf16x8 F;
   typedef Lay<bf16, D> L;
@@ -528,6 +545,23 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     }
   };
 
+  // Dropout keep bits of one 32-key block kb of the pair at step `step` (query
+  // rows qb0..qb0+31): bit i for register i, i.e. query qb0 + 8 (i / 4) +
+  // 4 hf + i % 4 and key kp + 32 kb + l32.  Both waves of a pair draw them.
+  auto pair_keep_bits = [&](int kb, int qb0, int step) {
+    const int key = kp + 32 * kb + l32;
+    const uint32_t bhq = (uint32_t)(b * a.H + h0 + step / nq);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x4 x = philox4x32_10((uint32_t)key >> 2, (uint32_t)(qb0 + 8 * g4 + 4 * hf) >> 2, bhq,
+                                    a.drop.offset, a.drop.k0, a.drop.k1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(x[e], 8u * (key & 3), a.drop.t) << (4 * g4 + e);
+    }
+    return bits;
+  };
+
   typedef std::integral_constant<bool, false> Full;
   typedef std::integral_constant<bool, true> Any;
   if (w < 4) {
@@ -555,14 +589,22 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
         if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
         sv[i] = p;
       };
-      auto emit = [&](const f32x16& sv, F (&pf)[2], int kb) {
+      auto emit = [&](f32x16& sv, F (&pf)[2], int kb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          frag_from(pf[t], sv, 8 * t);
           f16x8 ph;  // P goes to the dS wave in fp16 (P is in [0, 1]; 11-bit significand)
           frag_from(ph, sv, 8 * t);
           *reinterpret_cast<f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16) = ph;
         }
+        // Dropout: dV takes the kept p (the dS wave draws the same mask itself).
+        if constexpr (DROP) {
+          const uint32_t bits = pair_keep_bits(kb, qb0, it);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!((bits >> i) & 1u)) sv[i] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) frag_from(pf[t], sv, 8 * t);
       };
       int rx = rx0;
       asm volatile("" : "+v"(rx));
@@ -657,7 +699,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     // exponentials, and its vector work while the P wave runs products.
     F ds[2][2];
     auto dk = [&](const char* tq) { cols_x_frag(tq, ds); };
-    auto dpds = [&](const char* to, const float* td, const char* tp) {
+    auto dpds = [&](const char* to, const float* td, const char* tp, int step) {
       f32x16 dp[2], nd;
       // The accumulators start at -D (the workspace holds -D per query row).
 #pragma unroll
@@ -666,20 +708,31 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = v[e];
       }
-      rows_x_kv(dp, to, nd);
+      rows_x_kv(dp, to, DROP ? f32x16{} : nd);
       // dS = P * (dP - D) as fma(P, dP - D, z) with an addend z = 0 that the
       // compiler cannot fold away: that form selects v_fma_mix_f32, which
       // reads the fp16 P directly (no separate conversion).
       float z = 0.f;
       asm volatile("" : "+v"(z));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t bits = 0;
+        if constexpr (DROP) bits = pair_keep_bits(kb, qbase(step), step);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) ds[kb][t][j] = (bf16)__builtin_fmaf((float)pv[j], dp[kb][8 * t + j], z);
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (DROP) {
+              // dS = P (dP keep/(1 - rate) - D)
+              const float k = ((bits >> (8 * t + j)) & 1u) ? a.drop.inv : 0.f;
+              ds[kb][t][j] = (bf16)((float)pv[j] * __builtin_fmaf(dp[kb][8 * t + j], k, nd[8 * t + j]));
+            } else {
+              ds[kb][t][j] = (bf16)__builtin_fmaf((float)pv[j], dp[kb][8 * t + j], z);
+            }
+          }
         }
+      }
     };
     // Interval 0: copies of step 1 only.
     if (1 < total) fetch(1, 1);
@@ -695,7 +748,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     for (int j = 0; j < total; ++j) {
       if (j + 2 < total) fetch(j + 2, (j + 2) & 3);
       dk(sQ[(j - 1) & 3]);
-      dpds(sO[j & 3], sD[j & 3], sP[j & 1][pr]);
+      dpds(sO[j & 3], sD[j & 3], sP[j & 1][pr], j);
       if (j + 1 < total) {
         wait_copies();
         __syncthreads();
@@ -706,7 +759,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 
   // Lane l32 of key block kb owns key kp + 32 kb + l32.
   const int which = w < 4 ? 1 : 0;  // 0: dK, 1: dV
-  const float sc = w < 4 ? 1.f : a.scale;
+  const float sc = w < 4 ? (DROP ? a.drop.inv : 1.f) : a.scale;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kp + 32 * kb + l32;
@@ -720,9 +773,9 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPairThreads, 2) void fa_bwd_dkdv_kernel_bf16(BwdArgs a) {
-  dkdv_pair_body<D, CAUSAL>(a);
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(kPairThreads, DROP ? 1 : 2) void fa_bwd_dkdv_kernel_bf16(BwdArgs a) {
+  dkdv_pair_body<D, CAUSAL, DROP>(a);
 }
 
 // Sums the nsplit float32 partials of dK and dV (in slice order) into dk / dv.
@@ -745,7 +798,7 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restr
 constexpr int kDqWavesBf16 = 8;
 constexpr int kKTile = 64;           // keys per streamed tile
 
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   constexpr int kQTile = 32 * NW, kThreads = 64 * NW;
   typedef typename Frag<T>::type F;
@@ -828,11 +881,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
         s = mfma_k16(kf, qf[ks], s);
         dp = mfma_k16(vf, of[ks], dp);
       }
+      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e.
+      uint32_t bits = 0;
+      if constexpr (DROP) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t c = (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hf) >> 2;
+          const uint32_t wd = drop_word_of_row(a.drop, c, myq, (uint32_t)bh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(wd, 8 * e, a.drop.t) << (4 * g + e);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
         if (MASK && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
-        dp[i] = p * (dp[i] + dd);
+        if constexpr (DROP) dp[i] = p * __builtin_fmaf(dp[i], ((bits >> i) & 1u) ? a.drop.inv : 0.f, dd);
+        else dp[i] = p * (dp[i] + dd);
       }
       // dQ^T += K^T dS^T, 16 keys per step.
 #pragma unroll
@@ -875,13 +940,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kDqWavesBf16, 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
-  dq_body<bf16, D, CAUSAL, kDqWavesBf16>(a, nqt);
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(64 * kDqWavesBf16, DROP ? 1 : 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
+  dq_body<bf16, D, CAUSAL, kDqWavesBf16, DROP>(a, nqt);
 }
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel_f32(BwdArgs a, int nqt) {
-  dq_body<float, D, CAUSAL, kWaves>(a, nqt);
+  dq_body<float, D, CAUSAL, kWaves, DROP>(a, nqt);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -900,10 +965,13 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
   constexpr int keys = sizeof(T) == 2 ? kPairKeys : kKeys;
   const int nkt = (p.N + keys - 1) / keys;
   const dim3 grid((unsigned)((long)nkt * p.B * p.Hkv * p.nsplit));
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL>), grid, dim3(kPairThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a);
+  if constexpr (sizeof(T) == 2) {
+    if (p.drop.on) hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL, true>), grid, dim3(kPairThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fa_bwd_dkdv_kernel_bf16<D, CAUSAL, false>), grid, dim3(kPairThreads), 0, stream, a);
+  } else {
+    if (p.drop.on) hipLaunchKernelGGL((fa_bwd_dkdv_kernel_f32<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((fa_bwd_dkdv_kernel_f32<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   const long n4 = (long)p.B * p.Hkv * p.N * D / 4;
@@ -918,10 +986,15 @@ hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
   const int qtile = 32 * (sizeof(T) == 2 ? kDqWavesBf16 : kWaves);
   const int nqt = (p.N + qtile - 1) / qtile;
   const dim3 grid((unsigned)((long)nqt * p.B * p.H));
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
-  else
-    hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL>), grid, dim3(kThreads), 0, stream, a, nqt);
+  if constexpr (sizeof(T) == 2) {
+    if (p.drop.on)
+      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, true>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
+    else
+      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, false>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
+  } else {
+    if (p.drop.on) hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, a, nqt);
+    else hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, a, nqt);
+  }
   return hipGetLastError();
 }
 

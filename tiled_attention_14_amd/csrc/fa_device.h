@@ -349,4 +349,49 @@ __device__ __forceinline__ void xcd_map(int bid, int units, int& unit, int& slot
   }
 }
 
+// ---------------------------------------------------------------- dropout
+// Randomness of the dropout on P: Philox4x32-10 (Salmon, Moraes, Dror and
+// Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  One call
+// covers a 4 x 4 block of one head's score matrix, query rows 4a..4a+3 and keys
+// 4c..4c+3: counter (c, a, b*H + h, offset) under the 64-bit seed.  Word r of
+// the result belongs to query 4a + r and its byte e (little-endian) to key
+// 4c + e; an element is kept when its byte is >= t, so the drop rate is t/256.
+struct DropArgs {
+  uint32_t k0, k1;  // seed: low and high word
+  uint32_t offset;  // fourth counter word
+  uint32_t t;       // byte threshold, 1..255
+  float inv;        // 256 / (256 - t): the inverted-dropout scale
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The block of keys 4c..4c+3 for query row q: its four bytes, one word.
+__device__ __forceinline__ uint32_t drop_word_of_row(const DropArgs& d, uint32_t c, int q, uint32_t bh) {
+  const u32x4 x = philox4x32_10(c, (uint32_t)q >> 2, bh, d.offset, d.k0, d.k1);
+  const int r = q & 3;
+  return r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
+}
+
+__device__ __forceinline__ bool drop_keep(uint32_t word, uint32_t shift, uint32_t t) {
+  return ((word >> shift) & 0xffu) >= t;
+}
+
 }  // namespace fa

@@ -68,6 +68,7 @@ struct FwdArgs {
   void* o; float* lse;
   int B, H, Hkv, N, nqt;
   float c;  // scale * log2(e)
+  DropArgs drop;
 };
 
 // Operand type of the P V product: fp16 for bf16 inputs, fp32 for fp32 inputs.
@@ -75,7 +76,7 @@ template <typename T> struct PvFrag;
 template <> struct PvFrag<bf16> { typedef f16x8 type; };
 template <> struct PvFrag<float> { typedef f32x8 type; };
 
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int kWaves = NW, kThreads = 64 * NW, kBr = 32 * NW;
   typedef typename Frag<T>::type F;
@@ -142,6 +143,23 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  // Dropout: keep bit (16 kb + i) for the score in register i of key block kb
+  // (key k0 + 32 kb + 8 (i / 4) + 4 hf + i % 4, query myq); one generator call
+  // per four keys of this lane's row.
+  auto keep_bits = [&](int k0) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t c = (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hf) >> 2;
+        const uint32_t wd = drop_word_of_row(a.drop, c, myq, (uint32_t)bh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(wd, 8 * e, a.drop.t) << (16 * kb + 4 * g + e);
+      }
+    return bits;
+  };
 
   // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK selects
   // the general form (causal diagonal, ragged tail, waves with nothing to do);
@@ -224,6 +242,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         ts = probs();
       }
       lsum += ts;
+      if constexpr (DROP) {
+        // The row sum keeps every p; the product sees the kept ones.
+        const uint32_t bits = keep_bits(k0);
+#pragma unroll
+        for (int t = 0; t < kBc / 16; ++t)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (!((bits >> (8 * t + u)) & 1u)) pfs[t][u] = (_Float16)0.f;
+      }
     } else {
       raise_max();
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -236,6 +263,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
           ps[i & 3] += p;
         }
       lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      if constexpr (DROP) {
+        const uint32_t bits = keep_bits(k0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (!((bits >> (16 * kb + i)) & 1u)) s[kb][i] = 0.f;
+      }
 #pragma unroll
       for (int t = 0; t < kBc / 16; ++t) frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
     }
@@ -278,17 +313,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   }
 
   lsum += other_half(lsum);
-  store_rows<T, D>(reinterpret_cast<T*>(a.o) + (size_t)bh * slab, myq, N, acc, 1.f / lsum);
+  store_rows<T, D>(reinterpret_cast<T*>(a.o) + (size_t)bh * slab, myq, N, acc, (DROP ? a.drop.inv : 1.f) / lsum);
   if (hf == 0 && myq < N) a.lse[(size_t)bh * N + myq] = (m + __log2f(lsum)) * kLn2;
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWavesBf16, 2) void fa_fwd_kernel_bf16(FwdArgs a) {
-  fwd_body<bf16, D, CAUSAL, kWavesBf16>(a);
+// With dropout the generator's registers come on top of the tile's, so those
+// variants are built for one workgroup per CU.
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(64 * kWavesBf16, DROP ? 1 : 2) void fa_fwd_kernel_bf16(FwdArgs a) {
+  fwd_body<bf16, D, CAUSAL, kWavesBf16, DROP>(a);
 }
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64 * kWavesF32, 1) void fa_fwd_kernel_f32(FwdArgs a) {
-  fwd_body<float, D, CAUSAL, kWavesF32>(a);
+  fwd_body<float, D, CAUSAL, kWavesF32, DROP>(a);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -299,11 +336,15 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   constexpr int waves = sizeof(T) == 2 ? kWavesBf16 : kWavesF32;
   a.nqt = (p.N + 32 * waves - 1) / (32 * waves);
   a.c = p.scale * kLog2e;
+  a.drop = DropArgs{p.drop.k0, p.drop.k1, p.drop.offset, p.drop.t, p.drop.inv};
   const dim3 grid((unsigned)((long)a.nqt * p.B * p.H));
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL>), grid, dim3(64 * waves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL>), grid, dim3(64 * waves), 0, stream, a);
+  if constexpr (sizeof(T) == 2) {
+    if (p.drop.on) hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL, true>), grid, dim3(64 * waves), 0, stream, a);
+    else hipLaunchKernelGGL((fa_fwd_kernel_bf16<D, CAUSAL, false>), grid, dim3(64 * waves), 0, stream, a);
+  } else {
+    if (p.drop.on) hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL, true>), grid, dim3(64 * waves), 0, stream, a);
+    else hipLaunchKernelGGL((fa_fwd_kernel_f32<D, CAUSAL, false>), grid, dim3(64 * waves), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -15,6 +16,13 @@ constexpr int kDkdvKeysF32 = 128, kDkdvQRowsF32 = 64;
 inline int dkdv_keys(Dtype t) { return t == kBF16 ? kDkdvKeysBf16 : kDkdvKeysF32; }
 inline int dkdv_qrows(Dtype t) { return t == kBF16 ? kDkdvQRowsBf16 : kDkdvQRowsF32; }
 
+// Dropout on P (inverted scaling): the seed, the fourth counter word and the
+// byte threshold t (1..255) of the Philox mask; `on` false runs without it.
+struct DropParams {
+  bool on = false;
+  uint32_t k0 = 0, k1 = 0, offset = 0, t = 0;
+  float inv = 1.f;  // 256 / (256 - t)
+};
 struct FwdParams {
   const void* q; const void* k; const void* v;
   void* o; float* lse;
@@ -22,6 +30,7 @@ struct FwdParams {
   float scale;
   bool causal;
   Dtype dtype;
+  DropParams drop;
 };
 
 struct BwdParams {
@@ -35,7 +44,7 @@ struct BwdParams {
   int B, H, Hkv, N, d;
   float scale;
   bool causal;
-  Dtype dtype;
+  Dtype dtype;  DropParams drop;
 };
 
 // Attention of Nq query rows over Nk keys split into nsplit ranges of

@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
         L.fa_merge.restype = I
         L.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, P]
         L.fa_fwd_fp8.restype = I
+        U64, U32 = ctypes.c_ulonglong, ctypes.c_uint
+        L.fa_fwd_dropout.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, F, U64, U32, I, P]
+        L.fa_fwd_dropout.restype = I
+        L.fa_bwd_dropout.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, F, U64, U32, I, P, S, P]
+        L.fa_bwd_dropout.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -96,6 +101,21 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtyp
                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
                         int(bool(causal)), int(dtype), _ptr(workspace), int(workspace_bytes),
                         _stream(stream))
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, p_drop, seed, offset, dtype,
+                   stream=None) -> int:
+    return lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d, float(scale),
+                                int(bool(causal)), float(p_drop), int(seed), int(offset), int(dtype),
+                                _stream(stream))
+
+
+def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, p_drop, seed, offset,
+                   dtype, workspace, workspace_bytes, stream=None) -> int:
+    return lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                                int(bool(causal)), float(p_drop), int(seed), int(offset), int(dtype),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def fa_bwd_preprocess(o, dO, lse, B, H, Hkv, N, d, dtype, workspace, workspace_bytes, stream=None) -> int:
@@ -199,6 +219,40 @@ def backward(q, k, v, o, do, lse, scale=None, causal=False, stream=None, ws=None
         ws = workspace(B, H, Hkv, N, d, dt, q.device)
     _, addr, n = ws
     st = fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, N, d, s, causal, dt, addr, n, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return dq, dk, dv
+
+
+def forward_dropout(q, k, v, p_drop, seed, offset=0, scale=None, causal=False, stream=None):
+    """(o, lse) with dropout of rate ``p_drop`` on the probabilities (mask drawn
+    from ``seed`` and ``offset``; see fa_fwd_dropout in include/fa.h)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, Hkv, N, d, dt = _dims(q, k)
+    s = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd_dropout(q, k, v, o, lse, B, H, Hkv, N, d, s, causal, p_drop, seed, offset, dt, stream)
+    if st != FA_OK:
+        raise FAError(st)
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, scale=None, causal=False, stream=None,
+                     ws=None):
+    """(dq, dk, dv) of sum(do * o) for the o of :func:`forward_dropout` with the
+    same rate, seed and offset (the mask is regenerated, not stored)."""
+    import torch
+    _check_tensors(q, k, v, o, do, lse)
+    B, H, Hkv, N, d, dt = _dims(q, k)
+    s = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q); dk = torch.empty_like(k); dv = torch.empty_like(v)
+    if ws is None:
+        ws = workspace(B, H, Hkv, N, d, dt, q.device)
+    _, addr, n = ws
+    st = fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, N, d, s, causal, p_drop, seed, offset, dt,
+                        addr, n, stream)
     if st != FA_OK:
         raise FAError(st)
     return dq, dk, dv
