@@ -183,6 +183,52 @@ def fp8_leg(dev, calls=50, warmup=10):
             "bound": "mfma", "peak": PEAK_FP8_TFLOPS, "frac": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 
+def dropout_leg(dev, calls=20, warmup=5, p_drop=0.1):
+    """Times fa_fwd_dropout + fa_bwd_dropout (rate p_drop, one seed and offset)
+    on the headline shape with HIP events on the launch stream; the rate is the
+    step's algorithmic matrix flops (those of attention without dropout)
+    against the dense bf16 peak, beside the plain step's."""
+    import torch
+    from tiled_attention_14_amd import fa, synth
+    w = synth.WORKLOADS[synth.HEADLINE]
+    inp = synth.make_inputs(w)
+    t = {n: torch.from_numpy(inp.bits[n].view("int16")).view(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do")}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws_buf, addr, nbytes = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, fa.FA_BF16, dev)  # ws_buf owns the memory
+    stream = torch.cuda.current_stream()
+    args = (w.B, w.H, w.Hkv, w.N, w.d, w.scale, w.causal, p_drop, 0x5EED, 0)
+
+    def fwd():
+        if fa.fa_fwd_dropout(t["q"], t["k"], t["v"], o, lse, *args, fa.FA_BF16, stream) != fa.FA_OK:
+            raise RuntimeError("fa_fwd_dropout failed")
+
+    def bwd():
+        if fa.fa_bwd_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, *args, fa.FA_BF16, addr, nbytes,
+                             stream) != fa.FA_OK:
+            raise RuntimeError("fa_bwd_dropout failed")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls
+
+    ms_f, ms_b = timed(fwd), timed(bwd)
+    f_all = flops(w)[2]
+    tf = f_all / ((ms_f + ms_b) * 1e-3) / 1e12
+    log(f"[bench] dropout p={p_drop} {w.name}: fwd {ms_f:.4f} ms, bwd {ms_b:.4f} ms, {tf:.1f} TFLOP/s")
+    return {"workload": w.name, "p_drop": p_drop, "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "tflops": round(tf, 2), "bound": "mfma", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     from tiled_attention_14_amd import synth
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -191,7 +237,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode and fp8 legs (headline only)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode, fp8 and dropout legs (headline only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -322,6 +368,7 @@ def main():
     }
     out["decode"] = None if args.no_decode else decode_leg(dev)
     out["fp8_forward"] = None if args.no_decode else fp8_leg(dev)
+    out["dropout"] = None if args.no_decode else dropout_leg(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
