@@ -547,19 +547,13 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 
   // Dropout keep bits of one 32-key block kb of the pair at step `step` (query
   // rows qb0..qb0+31): bit i for register i, i.e. query qb0 + 8 (i / 4) +
-  // 4 hf + i % 4 and key kp + 32 kb + l32.  Both waves of a pair draw them.
+  // 4 hf + i % 4 and key kp + 32 kb + l32.  Both waves of a pair draw them;
+  // within a wave the lanes of keys 4c..4c+3 share each generator block.
   auto pair_keep_bits = [&](int kb, int qb0, int step) {
     const int key = kp + 32 * kb + l32;
+    const int r = lane & 3;  // == key % 4
     const uint32_t bhq = (uint32_t)(b * a.H + h0 + step / nq);
-    uint32_t bits = 0;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const u32x4 x = philox4x32_10((uint32_t)key >> 2, (uint32_t)(qb0 + 8 * g4 + 4 * hf) >> 2, bhq,
-                                    a.drop.offset, a.drop.k0, a.drop.k1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(x[e], 8u * (key & 3), a.drop.t) << (4 * g4 + e);
-    }
-    return bits;
+    return keep_cols_quad(a.drop, (uint32_t)key >> 2, (uint32_t)(qb0 + 8 * r + 4 * hf) >> 2, bhq, r);
   };
 
   typedef std::integral_constant<bool, false> Full;
@@ -881,16 +875,13 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
         s = mfma_k16(kf, qf[ks], s);
         dp = mfma_k16(vf, of[ks], dp);
       }
-      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e.
+      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e
+      // (one generator draw per lane, shared by the lanes of rows 4a..4a+3).
       uint32_t bits = 0;
       if constexpr (DROP) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t c = (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hf) >> 2;
-          const uint32_t wd = drop_word_of_row(a.drop, c, myq, (uint32_t)bh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(wd, 8 * e, a.drop.t) << (4 * g + e);
-        }
+        const int r = lane & 3;
+        bits = keep_rows_quad(a.drop, (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2, (uint32_t)myq >> 2,
+                              (uint32_t)bh, r);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

@@ -394,4 +394,60 @@ __device__ __forceinline__ bool drop_keep(uint32_t word, uint32_t shift, uint32_
   return ((word >> shift) & 0xffu) >= t;
 }
 
+// Keep bits of the four bytes of a word: bit e for byte e.
+__device__ __forceinline__ uint32_t keep_nibble(uint32_t w, uint32_t t) {
+  return (uint32_t)(((w) & 0xffu) >= t) | ((uint32_t)(((w >> 8) & 0xffu) >= t) << 1) |
+         ((uint32_t)(((w >> 16) & 0xffu) >= t) << 2) | ((uint32_t)((w >> 24) >= t) << 3);
+}
+
+// Value of lane (lane ^ X) within each group of four lanes (DPP quad_perm).
+template <int X>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v) {
+  if constexpr (X == 0) return v;
+  constexpr int ctrl = X == 1 ? 0xB1 : X == 2 ? 0x4E : 0x1B;  // [1,0,3,2], [2,3,0,1], [3,2,1,0]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t pick4(const u32x4& x, int i) {
+  return i == 0 ? x[0] : i == 1 ? x[1] : i == 2 ? x[2] : x[3];
+}
+
+// The four lanes of a quad (r = lane % 4) share four generator blocks: lane r
+// draws block r, then three exchanges (lane r reads lane r ^ X) hand each
+// lane its share of all four.  The whole wave must be active.
+//
+// keep_rows_quad: lane r holds query row 4a + r and needs, of block g (key
+// block cr - 2 (r - g), i.e. keys 8 apart between blocks), word r: the keys
+// of its row.  `cr` is the key block of block r.  Bit 4 g + e: key
+// 4 c_g + e kept.
+__device__ __forceinline__ uint32_t keep_rows_quad(const DropArgs& d, uint32_t cr, uint32_t a, uint32_t bh,
+                                                   int r) {
+  const u32x4 x = philox4x32_10(cr, a, bh, d.offset, d.k0, d.k1);
+  uint32_t bits = keep_nibble(pick4(x, r), d.t) << (4 * r);
+  bits |= keep_nibble(quad_xor<1>(pick4(x, r ^ 1)), d.t) << (4 * (r ^ 1));
+  bits |= keep_nibble(quad_xor<2>(pick4(x, r ^ 2)), d.t) << (4 * (r ^ 2));
+  bits |= keep_nibble(quad_xor<3>(pick4(x, r ^ 3)), d.t) << (4 * (r ^ 3));
+  return bits;
+}
+
+// Byte j of each word of x, packed: byte e of the result is byte j of x[e].
+__device__ __forceinline__ uint32_t bytes_at(const u32x4& x, int j) {
+  const uint32_t sh = 8u * (uint32_t)j;
+  return ((x[0] >> sh) & 0xffu) | (((x[1] >> sh) & 0xffu) << 8) | (((x[2] >> sh) & 0xffu) << 16) |
+         (((x[3] >> sh) & 0xffu) << 24);
+}
+
+// keep_cols_quad: lane r holds key 4c + r and needs, of block g (query block
+// ar - 2 (r - g)), byte r of each word: the four queries of that block.  `ar`
+// is the query block of block r.  Bit 4 g + e: query 4 a_g + e kept.
+__device__ __forceinline__ uint32_t keep_cols_quad(const DropArgs& d, uint32_t c, uint32_t ar, uint32_t bh,
+                                                   int r) {
+  const u32x4 x = philox4x32_10(c, ar, bh, d.offset, d.k0, d.k1);
+  uint32_t bits = keep_nibble(bytes_at(x, r), d.t) << (4 * r);
+  bits |= keep_nibble(quad_xor<1>(bytes_at(x, r ^ 1)), d.t) << (4 * (r ^ 1));
+  bits |= keep_nibble(quad_xor<2>(bytes_at(x, r ^ 2)), d.t) << (4 * (r ^ 2));
+  bits |= keep_nibble(quad_xor<3>(bytes_at(x, r ^ 3)), d.t) << (4 * (r ^ 3));
+  return bits;
+}
+
 }  // namespace fa

@@ -145,19 +145,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   // Dropout: keep bit (16 kb + i) for the score in register i of key block kb
-  // (key k0 + 32 kb + 8 (i / 4) + 4 hf + i % 4, query myq); one generator call
-  // per four keys of this lane's row.
+  // (key k0 + 32 kb + 8 (i / 4) + 4 hf + i % 4, query myq).  The four lanes of
+  // rows 4a..4a+3 share each generator block: one draw per lane and key block.
   auto keep_bits = [&](int k0) {
+    const int r = lane & 3;
     uint32_t bits = 0;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t c = (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hf) >> 2;
-        const uint32_t wd = drop_word_of_row(a.drop, c, myq, (uint32_t)bh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bits |= (uint32_t)drop_keep(wd, 8 * e, a.drop.t) << (16 * kb + 4 * g + e);
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t cr = (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2;
+      bits |= keep_rows_quad(a.drop, cr, (uint32_t)myq >> 2, (uint32_t)bh, r) << (16 * kb);
+    }
     return bits;
   };
 
