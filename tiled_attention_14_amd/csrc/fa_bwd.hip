@@ -414,6 +414,9 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   constexpr int PB = 2 * 2 * 1024;  // P of one pair and step: 2 key blocks x 2 row groups x 1 KB
   __shared__ __attribute__((aligned(1024))) char sQ[4][TQ], sO[4][TQ], sP[2][kPairWaves / 2][PB];
   __shared__ __attribute__((aligned(256))) float sL[4][kPairRows], sD[4][kPairRows];
+  // Dropout: the P wave's keep bits of a step (both key blocks), per lane,
+  // handed to the dS wave beside P.
+  __shared__ __attribute__((aligned(256))) uint32_t sM[2][kPairWaves / 2][DROP ? 64 : 1];
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -547,8 +550,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 
   // Dropout keep bits of one 32-key block kb of the pair at step `step` (query
   // rows qb0..qb0+31): bit i for register i, i.e. query qb0 + 8 (i / 4) +
-  // 4 hf + i % 4 and key kp + 32 kb + l32.  Both waves of a pair draw them;
-  // within a wave the lanes of keys 4c..4c+3 share each generator block.
+  // 4 hf + i % 4 and key kp + 32 kb + l32.  The P wave draws them (the lanes
+  // of keys 4c..4c+3 share each generator block) and hands them on in sM.
   auto pair_keep_bits = [&](int kb, int qb0, int step) {
     const int key = kp + 32 * kb + l32;
     const int r = lane & 3;  // == key % 4
@@ -583,6 +586,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
         if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
         sv[i] = p;
       };
+      uint32_t mbits = 0;
       auto emit = [&](f32x16& sv, F (&pf)[2], int kb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -590,9 +594,11 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
           frag_from(ph, sv, 8 * t);
           *reinterpret_cast<f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16) = ph;
         }
-        // Dropout: dV takes the kept p (the dS wave draws the same mask itself).
+        // Dropout: dV takes the kept p; the keep bits go to the dS wave too.
         if constexpr (DROP) {
           const uint32_t bits = pair_keep_bits(kb, qb0, it);
+          mbits |= bits << (16 * kb);
+          if (kb == 1) sM[it & 1][pr][lane] = mbits;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (!((bits >> i) & 1u)) sv[i] = 0.f;
@@ -693,7 +699,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     // exponentials, and its vector work while the P wave runs products.
     F ds[2][2];
     auto dk = [&](const char* tq) { cols_x_frag(tq, ds); };
-    auto dpds = [&](const char* to, const float* td, const char* tp, int step) {
+    auto dpds = [&](const char* to, const float* td, const char* tp, const uint32_t* tm) {
       f32x16 dp[2], nd;
       // The accumulators start at -D (the workspace holds -D per query row).
 #pragma unroll
@@ -711,7 +717,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t bits = 0;
-        if constexpr (DROP) bits = pair_keep_bits(kb, qbase(step), step);
+        if constexpr (DROP) bits = tm[lane] >> (16 * kb);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
@@ -742,7 +748,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     for (int j = 0; j < total; ++j) {
       if (j + 2 < total) fetch(j + 2, (j + 2) & 3);
       dk(sQ[(j - 1) & 3]);
-      dpds(sO[j & 3], sD[j & 3], sP[j & 1][pr], j);
+      dpds(sO[j & 3], sD[j & 3], sP[j & 1][pr], sM[j & 1][pr]);
       if (j + 1 < total) {
         wait_copies();
         __syncthreads();
