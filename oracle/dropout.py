@@ -91,8 +91,12 @@ def drop_threshold(p_drop):
     return t, (256 - t) / 256.0
 
 
-def random_bytes(B, H, Nq, Nk, seed, offset):
-    """The 8 random bits of every score element: uint8 [B, H, Nq, Nk]."""
+def random_bytes(B, H, Nq, Nk, seed, offset, bh=None):
+    """The 8 random bits of every score element: uint8 [B, H, Nq, Nk].  With
+    ``bh`` (B = H = 1 only) the single head drawn is head b*H + h = bh of a
+    larger tensor."""
+    if bh is not None and (B, H) != (1, 1):
+        raise ValueError("bh selects one head: B and H must be 1")
     seed = int(seed)
     key = np.array([seed & _MASK32, (seed >> 32) & _MASK32], dtype=np.uint32)
     na, nc = (Nq + 3) // 4, (Nk + 3) // 4
@@ -100,17 +104,18 @@ def random_bytes(B, H, Nq, Nk, seed, offset):
     out = np.empty((B, H, 4 * na, 4 * nc), dtype=np.uint8)
     for b in range(B):
         for h in range(H):
-            ctr = np.stack([c, a, np.full_like(a, b * H + h), np.full_like(a, int(offset))], axis=-1)
+            head = b * H + h if bh is None else int(bh)
+            ctr = np.stack([c, a, np.full_like(a, head), np.full_like(a, int(offset))], axis=-1)
             words = philox4x32_10(ctr.astype(np.uint32), key)       # [na, nc, 4]: word r -> query 4a+r
             by = words.view(np.uint8).reshape(na, nc, 4, 4)          # [a, c, r, e] (little-endian bytes)
             out[b, h] = by.transpose(0, 2, 1, 3).reshape(4 * na, 4 * nc)
     return out[:, :, :Nq, :Nk]
 
 
-def keep_mask(B, H, Nq, Nk, p_drop, seed, offset):
+def keep_mask(B, H, Nq, Nk, p_drop, seed, offset, bh=None):
     """0/1 keep mask (float64) and the keep probability."""
     t, keep = drop_threshold(p_drop)
-    return (random_bytes(B, H, Nq, Nk, seed, offset) >= t).astype(np.float64), keep
+    return (random_bytes(B, H, Nq, Nk, seed, offset, bh) >= t).astype(np.float64), keep
 
 
 def _setup(q, k, v, causal):
@@ -135,24 +140,25 @@ def _probs(q, k, scale, causal):
     return e / l, (m + np.log(l))[..., 0]
 
 
-def attention_fwd_dropout_ref(q, k, v, scale, causal, p_drop, seed, offset):
-    """O [B,H,N,d] and LSE [B,H,N] of attention with dropout on P."""
+def attention_fwd_dropout_ref(q, k, v, scale, causal, p_drop, seed, offset, bh=None):
+    """O [B,H,N,d] and LSE [B,H,N] of attention with dropout on P.  ``bh``: the
+    inputs are one head (B = H = 1), head b*H + h = bh of a larger tensor."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, Hkv, N, d = _setup(q, k, v, causal)
-    M, keep = keep_mask(B, H, N, N, p_drop, seed, offset)
+    M, keep = keep_mask(B, H, N, N, p_drop, seed, offset, bh)
     P, lse = _probs(q, k, scale, causal)
     Z = P * M / keep
     O = np.einsum("bhij,bhjd->bhid", Z, np.repeat(v, H // Hkv, axis=1))
     return O, lse
 
 
-def attention_bwd_dropout_ref(q, k, v, do, scale, causal, p_drop, seed, offset):
+def attention_bwd_dropout_ref(q, k, v, do, scale, causal, p_drop, seed, offset, bh=None):
     """dQ, dK, dV of sum(O * dO) for the dropout forward above (GQA: K/V
-    gradients summed over the query heads of each group)."""
+    gradients summed over the query heads of each group; ``bh`` as there)."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, H, Hkv, N, d = _setup(q, k, v, causal)
     g = H // Hkv
-    M, keep = keep_mask(B, H, N, N, p_drop, seed, offset)
+    M, keep = keep_mask(B, H, N, N, p_drop, seed, offset, bh)
     P, _ = _probs(q, k, scale, causal)
     kk, vv = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
     Z = P * M / keep

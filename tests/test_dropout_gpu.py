@@ -12,6 +12,8 @@ through the C ABI) with the float64 dropout oracle of ``oracle/dropout.py``.
   within max(1e-2, 1.05 u (attn(|V|) + |O|) + 1e-5), u = 2^-8, attn(|V|)
   being the oracle's dropout attention of |V|; dQ/dK/dV relative L2 2e-2).
 * Rate 0 runs the plain path; LSE does not depend on the mask.
+* The benchmarked size (B=2, H=32, N=4096, d=128, causal, rate 0.1) run
+  whole, two heads compared in full (O 1e-2, LSE 1e-3, gradients 2e-2).
 """
 import numpy as np
 import pytest
@@ -108,3 +110,20 @@ def test_rate_zero_is_the_plain_path_and_lse_ignores_the_mask():
     assert not torch.equal(o0, o2)
     _, L = attention_fwd_ref(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.scale, True)
     assert float(np.max(np.abs(host64(l2) - L))) <= 1e-3
+
+
+@pytest.mark.parametrize("b,h", [(0, 5), (1, 31)])
+def test_dropout_at_the_benchmarked_size(b, h):
+    # The benchmark's dropout leg: the 7B-shaped causal layer (B=2, H=32,
+    # N=4096, d=128, bf16), rate 0.1, seed 0x5EED, offset 0, run whole; two
+    # heads compared in full with the bars of the named bf16 workloads.
+    w = synth.WORKLOADS[synth.HEADLINE]
+    assert (w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.causal) == (2, 32, 32, 4096, 128, "bf16", True)
+    p, seed, off = 0.1, 0x5EED, 0
+    inp, got = _run(w, p, seed, off)
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    q, k, v, do = (inp.f64(n)[sl] for n in ("q", "k", "v", "do"))
+    O, L = attention_fwd_dropout_ref(q, k, v, w.scale, True, p, seed, off, bh=b * w.H + h)
+    dq, dk, dv = attention_bwd_dropout_ref(q, k, v, do, w.scale, True, p, seed, off, bh=b * w.H + h)
+    one = synth.Workload(f"{w.name}_head_{b}_{h}", 1, 1, 1, w.N, w.d, "bf16", True)
+    check(one, {n: x[sl] for n, x in got.items()}, {"o": O, "lse": L, "dq": dq, "dk": dk, "dv": dv}, "dropout-full")

@@ -131,3 +131,23 @@ def test_gradients_against_finite_differences(causal):
             plus[which][idx] += h; minus[which][idx] -= h
             num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
         np.testing.assert_allclose(grad, num, rtol=0, atol=1e-7)
+
+
+def test_single_head_draw_is_that_head_of_the_full_draw():
+    full = random_bytes(2, 3, 9, 14, 0xABCDEF, 4)
+    for b in range(2):
+        for h in range(3):
+            assert np.array_equal(random_bytes(1, 1, 9, 14, 0xABCDEF, 4, bh=b * 3 + h)[0, 0], full[b, h])
+    q, k, v, do = _inputs(2, 3, 3, 9, 4, 6)
+    O, L = attention_fwd_dropout_ref(q, k, v, 0.4, True, 0.3, 0xABCDEF, 4)
+    g = attention_bwd_dropout_ref(q, k, v, do, 0.4, True, 0.3, 0xABCDEF, 4)
+    b, h = 1, 2
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    O1, L1 = attention_fwd_dropout_ref(q[sl], k[sl], v[sl], 0.4, True, 0.3, 0xABCDEF, 4, bh=b * 3 + h)
+    g1 = attention_bwd_dropout_ref(q[sl], k[sl], v[sl], do[sl], 0.4, True, 0.3, 0xABCDEF, 4, bh=b * 3 + h)
+    np.testing.assert_array_equal(O1[0, 0], O[b, h])
+    np.testing.assert_array_equal(L1[0, 0], L[b, h])
+    for x1, x in zip(g1, g):
+        np.testing.assert_allclose(x1[0, 0], x[b, h], rtol=0, atol=1e-13)
+    with pytest.raises(ValueError):
+        random_bytes(2, 1, 4, 4, 0, 0, bh=1)
