@@ -213,16 +213,18 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const int lim = mykey - qb0 - 4 * hf;
     const int qlim = N - 1 - qb0 - 4 * hf;
     auto softmax = [&](int mb) {
+      // Dropout: bit 4 g4 + e for query qb0 + 32 mb + 8 g4 + 4 hf + e and this
+      // lane's key (the lanes of keys 4c..4c+3 share each generator block).
+      uint32_t bits = 0;
+      if constexpr (DROP) {
+        const int r = lane & 3;  // == mykey % 4
+        bits = keep_cols_quad(a.drop, (uint32_t)mykey >> 2, (uint32_t)(qb0 + mb * 32 + 8 * r + 4 * hf) >> 2, bhq, r);
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int ql0 = mb * 32 + 8 * g4 + 4 * hf;
         const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql0);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(sD + ql0);
-        // Dropout: the generator's block of queries qb0 + ql0 + 0..3 and this
-        // lane's key; word e belongs to query e, byte mykey % 4 to the key.
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (DROP) x = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qb0 + ql0) >> 2, bhq, a.drop.offset,
-                                              a.drop.k0, a.drop.k1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
@@ -232,7 +234,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             if ((CAUSAL && c < lim) || c > qlim) p = 0.f;
           }
           if constexpr (DROP) {
-            const bool keep = drop_keep(x[e], 8u * (mykey & 3), a.drop.t);
+            const bool keep = (bits >> i) & 1u;
             s[mb][i] = keep ? p : 0.f;
             dp[mb][i] = p * __builtin_fmaf(dp[mb][i], keep ? a.drop.inv : 0.f, dd[e]);
           } else {

@@ -383,17 +383,6 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return u32x4{c0, c1, c2, c3};
 }
 
-// The block of keys 4c..4c+3 for query row q: its four bytes, one word.
-__device__ __forceinline__ uint32_t drop_word_of_row(const DropArgs& d, uint32_t c, int q, uint32_t bh) {
-  const u32x4 x = philox4x32_10(c, (uint32_t)q >> 2, bh, d.offset, d.k0, d.k1);
-  const int r = q & 3;
-  return r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
-}
-
-__device__ __forceinline__ bool drop_keep(uint32_t word, uint32_t shift, uint32_t t) {
-  return ((word >> shift) & 0xffu) >= t;
-}
-
 // Keep bits of the four bytes of a word: bit e for byte e.
 __device__ __forceinline__ uint32_t keep_nibble(uint32_t w, uint32_t t) {
   return (uint32_t)(((w) & 0xffu) >= t) | ((uint32_t)(((w >> 8) & 0xffu) >= t) << 1) |
