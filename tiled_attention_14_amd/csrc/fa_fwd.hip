@@ -314,8 +314,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   if (hf == 0 && myq < N) a.lse[(size_t)bh * N + myq] = (m + __log2f(lsum)) * kLn2;
 }
 
-// With dropout the generator's registers come on top of the tile's, so those
-// variants are built for one workgroup per CU.
+// With dropout the generator's registers come on top of the tile's: those
+// variants ask for one wave per SIMD at least (the second bound), which lets
+// the compiler go past 256 registers if it chooses to.
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64 * kWavesBf16, DROP ? 1 : 2) void fa_fwd_kernel_bf16(FwdArgs a) {
   fwd_body<bf16, D, CAUSAL, kWavesBf16, DROP>(a);
