@@ -874,6 +874,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     // Two 32-key halves, so that only one half's S and dP are live at a time.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e
+      // (one generator draw per lane, shared by the lanes of rows 4a..4a+3),
+      // drawn before the products so that its integer work can issue between
+      // them.
+      uint32_t bits = 0;
+      if constexpr (DROP) {
+        const int r = lane & 3;
+        bits = keep_rows_quad(a.drop, (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2, (uint32_t)myq >> 2,
+                              (uint32_t)bh, r);
+      }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -882,14 +892,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
         rf.read(vf, sV, kb, ks);
         s = mfma_k16(kf, qf[ks], s);
         dp = mfma_k16(vf, of[ks], dp);
-      }
-      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e
-      // (one generator draw per lane, shared by the lanes of rows 4a..4a+3).
-      uint32_t bits = 0;
-      if constexpr (DROP) {
-        const int r = lane & 3;
-        bits = keep_rows_quad(a.drop, (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2, (uint32_t)myq >> 2,
-                              (uint32_t)bh, r);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

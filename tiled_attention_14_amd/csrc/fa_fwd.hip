@@ -164,6 +164,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   auto tile = [&](const char* sK, const char* sV, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (MASK && CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
+    // Dropout keep bits, drawn before the products so that the generator's
+    // integer work can issue between them.
+    uint32_t dbits = 0;
+    if constexpr (DROP) dbits = keep_bits(k0);
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -241,12 +245,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       lsum += ts;
       if constexpr (DROP) {
         // The row sum keeps every p; the product sees the kept ones.
-        const uint32_t bits = keep_bits(k0);
 #pragma unroll
         for (int t = 0; t < kBc / 16; ++t)
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            if (!((bits >> (8 * t + u)) & 1u)) pfs[t][u] = (_Float16)0.f;
+            if (!((dbits >> (8 * t + u)) & 1u)) pfs[t][u] = (_Float16)0.f;
       }
     } else {
       raise_max();
@@ -261,12 +264,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         }
       lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       if constexpr (DROP) {
-        const uint32_t bits = keep_bits(k0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (!((bits >> (16 * kb + i)) & 1u)) s[kb][i] = 0.f;
+            if (!((dbits >> (16 * kb + i)) & 1u)) s[kb][i] = 0.f;
       }
 #pragma unroll
       for (int t = 0; t < kBc / 16; ++t) frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
