@@ -11,6 +11,7 @@ through the C ABI) with the float64 dropout oracle of ``oracle/dropout.py``.
   square-attention tests (f32: 1e-5 * max(1, max |ref|); bf16: LSE 1e-3, O
   within max(1e-2, 1.05 u (attn(|V|) + |O|) + 1e-5), u = 2^-8, attn(|V|)
   being the oracle's dropout attention of |V|; dQ/dK/dV relative L2 2e-2).
+* Twelve seeded random cases (shape, rate, seed, offset) compared the same way.
 * Rate 0 runs the plain path; LSE does not depend on the mask.
 * The benchmarked size (B=2, H=32, N=4096, d=128, causal, rate 0.1) run
   whole, two heads compared in full (O 1e-2, LSE 1e-3, gradients 2e-2).
@@ -127,3 +128,23 @@ def test_dropout_at_the_benchmarked_size(b, h):
     dq, dk, dv = attention_bwd_dropout_ref(q, k, v, do, w.scale, True, p, seed, off, bh=b * w.H + h)
     one = synth.Workload(f"{w.name}_head_{b}_{h}", 1, 1, 1, w.N, w.d, "bf16", True)
     check(one, {n: x[sl] for n, x in got.items()}, {"o": O, "lse": L, "dq": dq, "dk": dk, "dv": dv}, "dropout-full")
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 3]))
+        out.append((str(rng.choice(["bf16", "f32"])), int(rng.choice([64, 128])), bool(rng.integers(2)),
+                    int(rng.integers(1, 3)), hkv * int(rng.choice([1, 2, 4])), hkv, int(rng.integers(1, 400)),
+                    float(rng.integers(1, 250)) / 256, int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 32))))
+    return out
+
+
+@pytest.mark.parametrize("dt,d,causal,B,H,Hkv,N,p,seed,offset", _random_cases(12, 9300), ids=lambda x: str(x))
+def test_dropout_random_shapes(dt, d, causal, B, H, Hkv, N, p, seed, offset):
+    # Seeded random shapes, rates, seeds and offsets, compared like the sweep.
+    w = synth.Workload("dropout_random", B, H, Hkv, N, d, dt, causal, seed=9400 + N + d + H)
+    inp, got = _run(w, p, seed, offset)
+    ref, floor = _refs(w, inp, p, seed, offset)
+    check(w, got, ref, "dropout-random", f32_scaled=True, o_floor=floor)
