@@ -874,15 +874,15 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     // Two 32-key halves, so that only one half's S and dP are live at a time.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // Dropout: keep bit (4 g + e) for the key k0 + 32 kb + 8 g + 4 hf + e
+      // Dropout: byte e of word g for the key k0 + 32 kb + 8 g + 4 hf + e
       // (one generator draw per lane, shared by the lanes of rows 4a..4a+3),
       // drawn before the products so that its integer work can issue between
       // them.
-      uint32_t bits = 0;
+      u32x4 dw = u32x4{0u, 0u, 0u, 0u};
       if constexpr (DROP) {
         const int r = lane & 3;
-        bits = keep_rows_quad(a.drop, (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2, (uint32_t)myq >> 2,
-                              (uint32_t)bh, r);
+        dw = keep_words_rows_quad(a.drop, (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2, (uint32_t)myq >> 2,
+                                  (uint32_t)bh, r);
       }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -897,7 +897,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
         if (MASK && kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
-        if constexpr (DROP) dp[i] = p * __builtin_fmaf(dp[i], ((bits >> i) & 1u) ? a.drop.inv : 0.f, dd);
+        if constexpr (DROP) dp[i] = p * __builtin_fmaf(dp[i], byte_kept(dw[i >> 2], i & 3, a.drop.t) ? a.drop.inv : 0.f, dd);
         else dp[i] = p * (dp[i] + dd);
       }
       // dQ^T += K^T dS^T, 16 keys per step.

@@ -397,8 +397,13 @@ __device__ __forceinline__ uint32_t quad_xor(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
 }
 
+// x[i] for a lane-dependent i in 0..3, as two levels of selects on the bits
+// of i (with i = lane % 4 ^ constant, the two conditions are the same for
+// every call, so no compares are repeated).
 __device__ __forceinline__ uint32_t pick4(const u32x4& x, int i) {
-  return i == 0 ? x[0] : i == 1 ? x[1] : i == 2 ? x[2] : x[3];
+  const uint32_t lo = (i & 1) ? x[1] : x[0];
+  const uint32_t hi = (i & 1) ? x[3] : x[2];
+  return (i & 2) ? hi : lo;
 }
 
 // The four lanes of a quad (r = lane % 4) share four generator blocks: lane r
@@ -418,6 +423,20 @@ __device__ __forceinline__ uint32_t keep_rows_quad(const DropArgs& d, uint32_t c
   bits |= keep_nibble(quad_xor<3>(pick4(x, r ^ 3)), d.t) << (4 * (r ^ 3));
   return bits;
 }
+
+// The same exchange, returning the words themselves: element g is word r of
+// block g (the four bytes of this lane's row for keys 4 c_g .. 4 c_g + 3).
+// Round X brings block r ^ X; one more pass of selects puts them in block
+// order, so each byte is then tested where it is used.
+__device__ __forceinline__ u32x4 keep_words_rows_quad(const DropArgs& d, uint32_t cr, uint32_t a, uint32_t bh,
+                                                      int r) {
+  const u32x4 x = philox4x32_10(cr, a, bh, d.offset, d.k0, d.k1);
+  const u32x4 z = u32x4{pick4(x, r), quad_xor<1>(pick4(x, r ^ 1)), quad_xor<2>(pick4(x, r ^ 2)),
+                        quad_xor<3>(pick4(x, r ^ 3))};
+  return u32x4{pick4(z, r), pick4(z, r ^ 1), pick4(z, r ^ 2), pick4(z, r ^ 3)};
+}
+
+__device__ __forceinline__ bool byte_kept(uint32_t w, int e, uint32_t t) { return ((w >> (8 * e)) & 0xffu) >= t; }
 
 // Byte j of each word of x, packed: byte e of the result is byte j of x[e].
 __device__ __forceinline__ uint32_t bytes_at(const u32x4& x, int j) {

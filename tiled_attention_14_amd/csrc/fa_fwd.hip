@@ -144,18 +144,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  // Dropout: keep bit (16 kb + i) for the score in register i of key block kb
-  // (key k0 + 32 kb + 8 (i / 4) + 4 hf + i % 4, query myq).  The four lanes of
+  // Dropout: the random bytes of this lane's row; byte i % 4 of word
+  // [kb][i / 4] belongs to the score in register i of key block kb (key
+  // k0 + 32 kb + 8 (i / 4) + 4 hf + i % 4, query myq).  The four lanes of
   // rows 4a..4a+3 share each generator block: one draw per lane and key block.
-  auto keep_bits = [&](int k0) {
+  auto keep_words = [&](int k0, u32x4 (&dw)[2]) {
     const int r = lane & 3;
-    uint32_t bits = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint32_t cr = (uint32_t)(k0 + 32 * kb + 8 * r + 4 * hf) >> 2;
-      bits |= keep_rows_quad(a.drop, cr, (uint32_t)myq >> 2, (uint32_t)bh, r) << (16 * kb);
+      dw[kb] = keep_words_rows_quad(a.drop, cr, (uint32_t)myq >> 2, (uint32_t)bh, r);
     }
-    return bits;
   };
 
   // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK selects
@@ -166,8 +165,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if (MASK && CAUSAL && k0 > q0w + 31) return;  // every key of the tile is after every query of the wave
     // Dropout keep bits, drawn before the products so that the generator's
     // integer work can issue between them.
-    uint32_t dbits = 0;
-    if constexpr (DROP) dbits = keep_bits(k0);
+    u32x4 dw[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    if constexpr (DROP) keep_words(k0, dw);
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -248,8 +247,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
         for (int t = 0; t < kBc / 16; ++t)
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (!((dbits >> (8 * t + u)) & 1u)) pfs[t][u] = (_Float16)0.f;
+          for (int u = 0; u < 8; ++u) {
+            const int i = 8 * (t & 1) + u;  // register i of key block t / 2
+            if (!byte_kept(dw[t >> 1][i >> 2], i & 3, a.drop.t)) pfs[t][u] = (_Float16)0.f;
+          }
       }
     } else {
       raise_max();
@@ -268,7 +269,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (!((dbits >> (16 * kb + i)) & 1u)) s[kb][i] = 0.f;
+            if (!byte_kept(dw[kb][i >> 2], i & 3, a.drop.t)) s[kb][i] = 0.f;
       }
 #pragma unroll
       for (int t = 0; t < kBc / 16; ++t) frag_from(pfs[t], s[t >> 1], (t & 1) * 8);
