@@ -213,12 +213,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     const int lim = mykey - qb0 - 4 * hf;
     const int qlim = N - 1 - qb0 - 4 * hf;
     auto softmax = [&](int mb) {
-      // Dropout: bit 4 g4 + e for query qb0 + 32 mb + 8 g4 + 4 hf + e and this
-      // lane's key (the lanes of keys 4c..4c+3 share each generator block).
-      uint32_t bits = 0;
+      // Dropout: byte e of word g4 for query qb0 + 32 mb + 8 g4 + 4 hf + e and
+      // this lane's key (the lanes of keys 4c..4c+3 share each generator block).
+      u32x4 dw = u32x4{0u, 0u, 0u, 0u};
       if constexpr (DROP) {
         const int r = lane & 3;  // == mykey % 4
-        bits = keep_cols_quad(a.drop, (uint32_t)mykey >> 2, (uint32_t)(qb0 + mb * 32 + 8 * r + 4 * hf) >> 2, bhq, r);
+        dw = keep_words_cols_quad(a.drop, (uint32_t)mykey >> 2, (uint32_t)(qb0 + mb * 32 + 8 * r + 4 * hf) >> 2,
+                                  bhq, r);
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -234,7 +235,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
             if ((CAUSAL && c < lim) || c > qlim) p = 0.f;
           }
           if constexpr (DROP) {
-            const bool keep = (bits >> i) & 1u;
+            const bool keep = byte_kept(dw[g4], e, a.drop.t);
             s[mb][i] = keep ? p : 0.f;
             dp[mb][i] = p * __builtin_fmaf(dp[mb][i], keep ? a.drop.inv : 0.f, dd[e]);
           } else {
@@ -416,9 +417,9 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   constexpr int PB = 2 * 2 * 1024;  // P of one pair and step: 2 key blocks x 2 row groups x 1 KB
   __shared__ __attribute__((aligned(1024))) char sQ[4][TQ], sO[4][TQ], sP[2][kPairWaves / 2][PB];
   __shared__ __attribute__((aligned(256))) float sL[4][kPairRows], sD[4][kPairRows];
-  // Dropout: the P wave's keep bits of a step (both key blocks), per lane,
-  // handed to the dS wave beside P.
-  __shared__ __attribute__((aligned(256))) uint32_t sM[2][kPairWaves / 2][DROP ? 64 : 1];
+  // Dropout: the P wave's random bytes of a step (per key block and lane, as
+  // drawn: 16 queries x this lane's key), handed to the dS wave beside P.
+  __shared__ __attribute__((aligned(256))) u32x4 sM[2][kPairWaves / 2][2][DROP ? 64 : 1];
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -550,15 +551,16 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     }
   };
 
-  // Dropout keep bits of one 32-key block kb of the pair at step `step` (query
-  // rows qb0..qb0+31): bit i for register i, i.e. query qb0 + 8 (i / 4) +
-  // 4 hf + i % 4 and key kp + 32 kb + l32.  The P wave draws them (the lanes
-  // of keys 4c..4c+3 share each generator block) and hands them on in sM.
-  auto pair_keep_bits = [&](int kb, int qb0, int step) {
+  // Dropout random bytes of one 32-key block kb of the pair at step `step`
+  // (query rows qb0..qb0+31): byte i % 4 of word i / 4 for register i, i.e.
+  // query qb0 + 8 (i / 4) + 4 hf + i % 4 and key kp + 32 kb + l32.  The P wave
+  // draws them (the lanes of keys 4c..4c+3 share each generator block) and
+  // hands them on in sM.
+  auto pair_keep_words = [&](int kb, int qb0, int step) {
     const int key = kp + 32 * kb + l32;
     const int r = lane & 3;  // == key % 4
     const uint32_t bhq = (uint32_t)(b * a.H + h0 + step / nq);
-    return keep_cols_quad(a.drop, (uint32_t)key >> 2, (uint32_t)(qb0 + 8 * r + 4 * hf) >> 2, bhq, r);
+    return keep_words_cols_quad(a.drop, (uint32_t)key >> 2, (uint32_t)(qb0 + 8 * r + 4 * hf) >> 2, bhq, r);
   };
 
   typedef std::integral_constant<bool, false> Full;
@@ -588,7 +590,6 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
         if (MASK && 8 * (i >> 2) + (i & 3) < lim) p = 0.f;
         sv[i] = p;
       };
-      uint32_t mbits = 0;
       auto emit = [&](f32x16& sv, F (&pf)[2], int kb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -596,14 +597,13 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
           frag_from(ph, sv, 8 * t);
           *reinterpret_cast<f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16) = ph;
         }
-        // Dropout: dV takes the kept p; the keep bits go to the dS wave too.
+        // Dropout: dV takes the kept p; the random bytes go to the dS wave too.
         if constexpr (DROP) {
-          const uint32_t bits = pair_keep_bits(kb, qb0, it);
-          mbits |= bits << (16 * kb);
-          if (kb == 1) sM[it & 1][pr][lane] = mbits;
+          const u32x4 dw = pair_keep_words(kb, qb0, it);
+          sM[it & 1][pr][kb][lane] = dw;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (!((bits >> i) & 1u)) sv[i] = 0.f;
+            if (!byte_kept(dw[i >> 2], i & 3, a.drop.t)) sv[i] = 0.f;
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) frag_from(pf[t], sv, 8 * t);
@@ -701,7 +701,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     // exponentials, and its vector work while the P wave runs products.
     F ds[2][2];
     auto dk = [&](const char* tq) { cols_x_frag(tq, ds); };
-    auto dpds = [&](const char* to, const float* td, const char* tp, const uint32_t* tm) {
+    auto dpds = [&](const char* to, const float* td, const char* tp, const u32x4 (*tm)[DROP ? 64 : 1]) {
       f32x16 dp[2], nd;
       // The accumulators start at -D (the workspace holds -D per query row).
 #pragma unroll
@@ -718,8 +718,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
       asm volatile("" : "+v"(z));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        uint32_t bits = 0;
-        if constexpr (DROP) bits = tm[lane] >> (16 * kb);
+        u32x4 dw = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (DROP) dw = tm[kb][lane];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const f16x8 pv = *reinterpret_cast<const f16x8*>(tp + (2 * kb + t) * 1024 + lane * 16);
@@ -727,7 +727,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
           for (int j = 0; j < 8; ++j) {
             if constexpr (DROP) {
               // dS = P (dP keep/(1 - rate) - D)
-              const float k = ((bits >> (8 * t + j)) & 1u) ? a.drop.inv : 0.f;
+              const float k = byte_kept(dw[(8 * t + j) >> 2], j & 3, a.drop.t) ? a.drop.inv : 0.f;
               ds[kb][t][j] = (bf16)((float)pv[j] * __builtin_fmaf(dp[kb][8 * t + j], k, nd[8 * t + j]));
             } else {
               ds[kb][t][j] = (bf16)__builtin_fmaf((float)pv[j], dp[kb][8 * t + j], z);

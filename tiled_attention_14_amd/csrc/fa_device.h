@@ -383,12 +383,6 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return u32x4{c0, c1, c2, c3};
 }
 
-// Keep bits of the four bytes of a word: bit e for byte e.
-__device__ __forceinline__ uint32_t keep_nibble(uint32_t w, uint32_t t) {
-  return (uint32_t)(((w) & 0xffu) >= t) | ((uint32_t)(((w >> 8) & 0xffu) >= t) << 1) |
-         ((uint32_t)(((w >> 16) & 0xffu) >= t) << 2) | ((uint32_t)((w >> 24) >= t) << 3);
-}
-
 // Value of lane (lane ^ X) within each group of four lanes (DPP quad_perm).
 template <int X>
 __device__ __forceinline__ uint32_t quad_xor(uint32_t v) {
@@ -410,24 +404,12 @@ __device__ __forceinline__ uint32_t pick4(const u32x4& x, int i) {
 // draws block r, then three exchanges (lane r reads lane r ^ X) hand each
 // lane its share of all four.  The whole wave must be active.
 //
-// keep_rows_quad: lane r holds query row 4a + r and needs, of block g (key
-// block cr - 2 (r - g), i.e. keys 8 apart between blocks), word r: the keys
-// of its row.  `cr` is the key block of block r.  Bit 4 g + e: key
-// 4 c_g + e kept.
-__device__ __forceinline__ uint32_t keep_rows_quad(const DropArgs& d, uint32_t cr, uint32_t a, uint32_t bh,
-                                                   int r) {
-  const u32x4 x = philox4x32_10(cr, a, bh, d.offset, d.k0, d.k1);
-  uint32_t bits = keep_nibble(pick4(x, r), d.t) << (4 * r);
-  bits |= keep_nibble(quad_xor<1>(pick4(x, r ^ 1)), d.t) << (4 * (r ^ 1));
-  bits |= keep_nibble(quad_xor<2>(pick4(x, r ^ 2)), d.t) << (4 * (r ^ 2));
-  bits |= keep_nibble(quad_xor<3>(pick4(x, r ^ 3)), d.t) << (4 * (r ^ 3));
-  return bits;
-}
-
-// The same exchange, returning the words themselves: element g is word r of
-// block g (the four bytes of this lane's row for keys 4 c_g .. 4 c_g + 3).
+// keep_words_rows_quad: lane r holds query row 4a + r and needs, of block g
+// (key block cr - 2 (r - g), i.e. keys 8 apart between blocks), word r: the
+// bytes of its row for keys 4 c_g .. 4 c_g + 3.  `cr` is the key block of
+// block r.
 // Round X brings block r ^ X; one more pass of selects puts them in block
-// order, so each byte is then tested where it is used.
+// order (element g of the result), so each byte is tested where it is used.
 __device__ __forceinline__ u32x4 keep_words_rows_quad(const DropArgs& d, uint32_t cr, uint32_t a, uint32_t bh,
                                                       int r) {
   const u32x4 x = philox4x32_10(cr, a, bh, d.offset, d.k0, d.k1);
@@ -445,17 +427,16 @@ __device__ __forceinline__ uint32_t bytes_at(const u32x4& x, int j) {
          (((x[3] >> sh) & 0xffu) << 24);
 }
 
-// keep_cols_quad: lane r holds key 4c + r and needs, of block g (query block
-// ar - 2 (r - g)), byte r of each word: the four queries of that block.  `ar`
-// is the query block of block r.  Bit 4 g + e: query 4 a_g + e kept.
-__device__ __forceinline__ uint32_t keep_cols_quad(const DropArgs& d, uint32_t c, uint32_t ar, uint32_t bh,
-                                                   int r) {
+// keep_words_cols_quad: lane r holds key 4c + r and needs, of block g (query
+// block ar - 2 (r - g)), byte r of each word: the four queries of that block.
+// `ar` is the query block of block r.  Element g of the result packs them:
+// byte e is the byte of query 4 a_g + e.
+__device__ __forceinline__ u32x4 keep_words_cols_quad(const DropArgs& d, uint32_t c, uint32_t ar, uint32_t bh,
+                                                      int r) {
   const u32x4 x = philox4x32_10(c, ar, bh, d.offset, d.k0, d.k1);
-  uint32_t bits = keep_nibble(bytes_at(x, r), d.t) << (4 * r);
-  bits |= keep_nibble(quad_xor<1>(bytes_at(x, r ^ 1)), d.t) << (4 * (r ^ 1));
-  bits |= keep_nibble(quad_xor<2>(bytes_at(x, r ^ 2)), d.t) << (4 * (r ^ 2));
-  bits |= keep_nibble(quad_xor<3>(bytes_at(x, r ^ 3)), d.t) << (4 * (r ^ 3));
-  return bits;
+  const u32x4 z = u32x4{bytes_at(x, r), quad_xor<1>(bytes_at(x, r ^ 1)), quad_xor<2>(bytes_at(x, r ^ 2)),
+                        quad_xor<3>(bytes_at(x, r ^ 3))};
+  return u32x4{pick4(z, r), pick4(z, r ^ 1), pick4(z, r ^ 2), pick4(z, r ^ 3)};
 }
 
 }  // namespace fa
