@@ -71,6 +71,15 @@ typedef enum {
 /*
  * Forward pass.  Writes o = softmax(scale * q k^T) v and lse.
  * Inputs q, k, v; outputs o and lse (see layouts above).
+ *
+ * Input domain of FA_BF16: the P V product runs on the fp16 matrix cores
+ * (the pages' forward runs in fp16: "FlashAttention V2深度解析", section
+ * 性能调优技巧, 混合精度训练), with V converted from bf16 to fp16.  That
+ * conversion is exact for 2^-14 <= |v| <= 65280, the largest bfloat16 below
+ * fp16's overflow threshold; smaller magnitudes keep an absolute error below
+ * 2^-25.  Every element of v must satisfy |v| <= 65280: a larger one becomes
+ * inf and makes o inf or NaN while the call still returns FA_OK (values are
+ * not inspected).  FA_F32 has no such limit.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    void* o, float* lse,
@@ -179,7 +188,8 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
  * quantised to t/256); t == 0 runs fa_fwd / fa_bwd.  Otherwise the same
  * arguments, layouts, workspace, ownership and errors as fa_fwd and fa_bwd.
  * fa_bwd_dropout takes the O written by fa_fwd_dropout and returns the
- * gradients of sum(O * dO) for that same mask.
+ * gradients of sum(O * dO) for that same mask.  fa_fwd_dropout has fa_fwd's
+ * input domain: for FA_BF16 every |v| <= 65280.
  */
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Hkv, int N, int d,
@@ -219,6 +229,11 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v,
  * workgroups: short query blocks (the cache reuse of section 七 of the same
  * page) get their parallelism from the keys.
  *
+ * Input domain: as fa_fwd, for FA_BF16 every |v| <= 65280 (the kernel for
+ * more than 32 query rows per KV head runs P V in fp16; the one for at most
+ * 32 rows in bf16, which has no such limit, but callers cannot rely on which
+ * one runs).
+ *
  * `workspace`: device memory of at least fa_fwd_splitkv_workspace_size(...)
  * bytes for the same sizes and nsplit, 256-byte aligned, owned by the caller;
  * contents on entry do not matter.  Returns FA_ERR_WORKSPACE when it is
@@ -253,6 +268,14 @@ fa_status_t fa_merge(const float* o_parts, const float* lse_parts, void* o, floa
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(fa_status_t s);
+
+/*
+ * Identifies the sources this library was built from: 16 hex digits of a
+ * SHA-256 over its source files, this header and the compile flags (a static
+ * string, never NULL).  A binding compares it with the hash of the sources it
+ * ships with and refuses a stale binary.
+ */
+const char* fa_build_hash(void);
 
 #ifdef __cplusplus
 }

@@ -29,9 +29,9 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout", "fa_bwd_preprocess",
-                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_merge",
-                     "fa_status_string"]
+    assert names == ["fa_build_hash", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout", "fa_bwd_preprocess",
+                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
+                     "fa_fwd_splitkv_workspace_size", "fa_merge", "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -300,3 +300,11 @@ def test_dropout_null_and_misaligned_pointers(lib, i):
         ptrs = [P] * 9; ptrs[i] = bad
         assert _bwd_drop(0.2, ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
     assert _bwd_drop(0.2, ws=0) == fa.FA_ERR_WORKSPACE
+
+
+def test_build_hash_matches_the_sources(lib):
+    """The loaded library was built from the sources in this tree (fa.lib()
+    refuses it otherwise), and a changed source changes the hash."""
+    from tiled_attention_14_amd import build
+    assert lib.fa_build_hash().decode() == build.source_hash()
+    assert len(build.source_hash()) == 16

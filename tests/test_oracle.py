@@ -268,3 +268,47 @@ def test_workload_inputs_are_bf16_exact_and_seeded():
     x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5], dtype=np.float32)
     np.testing.assert_array_equal(synth.bf16_bits_to_f32(synth.bf16_round_bits(x)),
                                   np.array([1.0, 1 + 2 ** -6, -2.5], dtype=np.float32))
+
+
+# ---------------------------------------------------------------- large N (threaded, several row blocks)
+@pytest.mark.parametrize("causal", [False, True])
+def test_threaded_row_blocks_against_torch_float64_autograd(causal):
+    """N >= 1024 takes the oracle's per-head thread pool, and N = 1100 spans
+    three 512-row blocks (the last one ragged): the path that judges every
+    full-size GPU comparison.  GQA (4 query heads on 2 KV heads), both masks,
+    against PyTorch float64 autograd of the naive formula; the sampled-row
+    mode at the same size against the same autograd result."""
+    torch = pytest.importorskip("torch")
+    import oracle.attention as ar
+    assert 1100 >= 1024 and len(os.sched_getaffinity(0)) > 1, "the threaded branch must run"
+    assert 1100 > 2 * ar._ROW_BLOCK, "at least three row blocks"
+    rng = np.random.default_rng(41)
+    B, H, Hkv, N, d, s = 1, 4, 2, 1100, 16, 0.21
+    q, k, v, do = _rand(rng, B, H, Hkv, N, d, std=1.3)
+    O, LSE, dQ, dK, dV = attention_ref(q, k, v, do, s, causal)
+    tq = torch.tensor(q, requires_grad=True); tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    kr = tk.repeat_interleave(H // Hkv, dim=1); vr = tv.repeat_interleave(H // Hkv, dim=1)
+    S = s * torch.matmul(tq, kr.transpose(-1, -2))
+    if causal:
+        S = S.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    to = torch.matmul(torch.softmax(S, dim=-1), vr)
+    tlse = torch.logsumexp(S, dim=-1)
+    (to * torch.tensor(do)).sum().backward()
+    ref = [x.detach().numpy() for x in (to, tlse, tq.grad, tk.grad, tv.grad)]
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), (O, LSE, dQ, dK, dV), ref):
+        np.testing.assert_allclose(a, b, atol=1e-11, rtol=0, err_msg=name)
+    # Sampled rows (per head, unsorted, spanning all three blocks) in the same threaded branch.
+    rows = np.stack([rng.choice(N, 300, replace=False) for _ in range(B * H)]).reshape(B, H, 300)
+    krows = np.stack([rng.choice(N, 250, replace=False) for _ in range(B * Hkv)]).reshape(B, Hkv, 250)
+    Os, LSEs = attention_fwd_ref(q, k, v, s, causal, rows=rows)
+    dQs, dKs, dVs = attention_bwd_ref(q, k, v, do, s, causal, rows=rows, key_rows=krows)
+    for h in range(H):
+        r = rows[0, h]
+        np.testing.assert_allclose(Os[0, h], ref[0][0, h, r], atol=1e-11, rtol=0)
+        np.testing.assert_allclose(LSEs[0, h], ref[1][0, h, r], atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dQs[0, h], ref[2][0, h, r], atol=1e-11, rtol=0)
+    for h in range(Hkv):
+        r = krows[0, h]
+        np.testing.assert_allclose(dKs[0, h], ref[3][0, h, r], atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dVs[0, h], ref[4][0, h, r], atol=1e-11, rtol=0)

@@ -3,10 +3,16 @@
 Usage: ``python -m tiled_attention_14_amd.build`` (or ``build()`` from Python).
 Objects go to ``tiled_attention_14_amd/_build/``; the shared library is written
 next to this file so it travels with the source tree.
+
+Every compiler warning fails the build (the host pass's note that it does not
+know the device-only ``packed-fp32-ops`` feature is the one line filtered
+out).  The library embeds ``source_hash()`` of the sources and flags it was
+built from; ``fa.lib()`` refuses a library whose hash differs from the tree's.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -31,6 +37,21 @@ HIP_FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """sha256 (16 hex digits) of every library source, the public header and the
+    compile flags: what the built library must match."""
+    h = hashlib.sha256()
+    h.update(" ".join(HIP_FLAGS).encode())
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "fa.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -44,6 +65,8 @@ def _run(cmd):
                     if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if "warning" in out:
+        raise RuntimeError(f"compiler warnings (the build treats them as errors): {' '.join(cmd)}\n{out}")
     return out
 
 
@@ -51,10 +74,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    tag = source_hash()
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        extra = ["-x", "hip"] if src.endswith(".hip") else []
+        extra = ["-x", "hip"] if src.endswith(".hip") else [f'-DFA_SOURCE_HASH="{tag}"']
         jobs.append((obj, [hipcc, *HIP_FLAGS, *inc, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))

@@ -338,3 +338,5 @@ const char* fa_status_string(fa_status_t s) {
 }
 
 }  // extern "C"
+
+extern "C" const char* fa_build_hash(void) { return FA_SOURCE_HASH; }

@@ -120,6 +120,10 @@ struct Lay {
 // (wait_copies) and then synchronises before it reads what it copied.
 // Both operands are wave-uniform by construction; readfirstlane moves them to
 // scalar registers where the compiler computed them in vector registers.
+// The LDS destination goes through m0, a register the compiler reserves: each
+// copy saves m0, sets it, issues the load (which latches m0 at issue; the
+// compiler's own LDS-DMA sequences rewrite m0 right after the load the same
+// way) and restores it, so the asm changes no register the compiler owns.
 __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
@@ -131,12 +135,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
 }
 __device__ __forceinline__ void copy16_to_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc) : "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc));
 }
 __device__ __forceinline__ void copy4_to_lds(const u32x4& desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc) : "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc));
 }
 
 // NF (32 or 64) consecutive floats [row0, row0 + NF) of the vector behind

@@ -64,6 +64,13 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dropout.restype = I
         L.fa_status_string.argtypes = [I]
         L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_build_hash.argtypes = []
+        L.fa_build_hash.restype = ctypes.c_char_p
+        from tiled_attention_14_amd.build import source_hash
+        built, tree = L.fa_build_hash().decode(), source_hash()
+        if built != tree:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (hash {built}) than this tree holds "
+                               f"({tree}): rebuild it with `python -m tiled_attention_14_amd.build`")
         _lib = L
     return _lib
 
