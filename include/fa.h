@@ -65,7 +65,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad sizes, H % Hkv != 0, scale not finite and > 0 */
   FA_ERR_UNSUPPORTED = 2, /* d not in {64, 128}, unknown dtype                                   */
   FA_ERR_WORKSPACE = 3,   /* workspace null, misaligned or smaller than fa_bwd_workspace_size    */
-  FA_ERR_HIP = 4          /* a kernel launch failed                                              */
+  FA_ERR_HIP = 4,         /* a kernel launch failed                                              */
+  FA_ERR_TOO_LARGE = 5    /* fa_bwd_noalloc: the sizes need more than its fixed scratch holds    */
 } fa_status_t;
 
 /*
@@ -132,6 +133,26 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    int B, int H, int Hkv, int N, int d,
                    float scale, int causal, fa_dtype_t dtype,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_bwd without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (minus the workspace), layouts, results
+ * and errors as fa_bwd; the workspace is a fixed 32 MiB device array inside
+ * the library, one per GPU it runs on, held until the process ends (its
+ * device address is looked up on the first call on each device; nothing is
+ * allocated or freed by any call).  Sizes whose workspace
+ * (fa_bwd_workspace_size) exceeds 32 MiB return FA_ERR_TOO_LARGE and enqueue
+ * nothing.  Every call on one GPU shares that array and leaves its last
+ * contents there (nothing in it needs to start at zero): calls whose work
+ * overlaps on one GPU (other streams, other host threads without ordering)
+ * race on it and must be serialised by the caller.
+ */
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int B, int H, int Hkv, int N, int d,
+                           float scale, int causal, fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * The three phases of fa_bwd, callable one by one (same arguments, layouts,

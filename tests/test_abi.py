@@ -29,7 +29,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_build_hash", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout", "fa_bwd_preprocess",
+    assert names == ["fa_build_hash", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dropout", "fa_bwd_noalloc",
+                     "fa_bwd_preprocess",
                      "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_splitkv",
                      "fa_fwd_splitkv_workspace_size", "fa_merge", "fa_status_string"]
     raw = ctypes.CDLL(fa.LIB_PATH)
@@ -38,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(5):
+    for st in range(6):
         s = fa.fa_status_string(st)
         assert s.startswith("FA_OK" if st == 0 else "FA_ERR")
     assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
@@ -308,3 +309,39 @@ def test_build_hash_matches_the_sources(lib):
     from tiled_attention_14_amd import build
     assert lib.fa_build_hash().decode() == build.source_hash()
     assert len(build.source_hash()) == 16
+
+
+def _noalloc(**kw):
+    a = dict(GOOD); a.update(kw)
+    ptrs = a.pop("ptrs", [P] * 9)
+    return fa.fa_bwd_noalloc(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG), (dict(H=3, Hkv=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    # 64 x 32 x 4096 query rows need 64 MiB of workspace: more than the fixed scratch
+    (dict(B=64, H=32, Hkv=32, N=4096, d=128), fa.FA_ERR_TOO_LARGE),
+])
+def test_noalloc_rejects_before_any_device_call(lib, kw, status):
+    assert _noalloc(**kw) == status
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_noalloc_null_and_misaligned_pointers(lib, i):
+    ptrs = [P] * 9
+    ptrs[i] = None
+    assert _noalloc(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+    ptrs[i] = P + 8
+    assert _noalloc(ptrs=ptrs) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_limit_matches_the_workspace_rule(lib):
+    """The 32 MiB limit is the workspace fa_bwd would need for the same sizes."""
+    limit = 32 << 20
+    big = dict(B=64, H=32, Hkv=32, N=4096, d=128)
+    assert fa.fa_bwd_workspace_size(64, 32, 32, 4096, 128, fa.FA_BF16) > limit
+    assert fa.fa_bwd_workspace_size(2, 32, 32, 4096, 128, fa.FA_BF16) <= limit
+    assert "32 MiB" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
+    assert _noalloc(**big) == fa.FA_ERR_TOO_LARGE

@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_splitkv.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_splitkv.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip"]
 
 # Packed-fp32 VALU forms are disabled on purpose: only scalar fp32 VALU code is
 # generated.  Float atomics are lowered to the hardware instructions.

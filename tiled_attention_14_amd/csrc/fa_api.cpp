@@ -239,6 +239,20 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   return FA_OK;
 }
 
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                           float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  if (!all_aligned({q, k, v, o, dO, lse, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  fa_status_t st = check_shape(B, H, Hkv, N, d, dtype, scale);
+  if (st != FA_OK) return st;
+  const int ns = dkdv_nsplit(B, H, Hkv, N, causal != 0, dtype);
+  const size_t need = layout(B, H, Hkv, N, d, ns).total;
+  if (need > fa::kNoallocScratchBytes) return FA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  return fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, ws, need, stream);
+}
+
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, float scale, int causal, float p_drop, unsigned long long seed,
                            unsigned int offset, fa_dtype_t dtype, hipStream_t stream) {
@@ -333,6 +347,8 @@ const char* fa_status_string(fa_status_t s) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension or dtype not supported";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the sizes need more workspace than the fixed 32 MiB scratch of fa_bwd_noalloc holds";
   }
   return "FA_ERR_UNKNOWN";
 }

@@ -89,4 +89,9 @@ hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 
+// Size of the fixed device scratch of fa_bwd_noalloc, and its device address
+// on the current device (looked up on first use per device).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace fa

@@ -1,6 +1,6 @@
 """Thin Python binding of the C ABI in ``include/fa.h``.
 
-``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_fwd_splitkv``,
+``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_noalloc``, ``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_merge``,
 ``fa_bwd_dq``, ``fa_bwd_workspace_size`` and ``fa_status_string`` have
 the C names and argument order; pointer arguments accept an integer device
@@ -17,7 +17,7 @@ import math
 import os
 
 FA_BF16, FA_F32 = 0, 1
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_TOO_LARGE = range(6)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_size.restype = S
         L.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         L.fa_bwd.restype = I
+        L.fa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+        L.fa_bwd_noalloc.restype = I
         L.fa_bwd_preprocess.argtypes = [P, P, P, I, I, I, I, I, I, P, S, P]
         L.fa_bwd_preprocess.restype = I
         L.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
@@ -108,6 +110,12 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtyp
                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
                         int(bool(causal)), int(dtype), _ptr(workspace), int(workspace_bytes),
                         _stream(stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, stream=None) -> int:
+    return lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale),
+                                int(bool(causal)), int(dtype), _stream(stream))
 
 
 def fa_fwd_dropout(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, p_drop, seed, offset, dtype,
