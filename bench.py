@@ -2,10 +2,14 @@
 """Benchmark of exact attention forward + backward on one MI355X (gfx950).
 
 One step is one pass of the whole path on one batch of synthetic input that is
-already resident in HBM: ``fa_fwd`` followed by the three backward phases
-(``fa_bwd_preprocess``, ``fa_bwd_dkdv``, ``fa_bwd_dq``, i.e. ``fa_bwd``),
-all on one stream.  W untimed warm-up steps, then exactly K timed steps
-bracketed by ``torch.cuda.synchronize()``.  Prints ONE JSON line on stdout.
+already resident in HBM: ``fa_fwd`` followed by the backward phases of
+``fa_bwd`` (``fa_bwd_dq``, which also forms the row terms D and lse * log2 e,
+then ``fa_bwd_dkdv``), all on one stream.  W untimed warm-up steps; then K
+steps with HIP events between the kernels, which bring the shader clock to
+its loaded level (that takes some tens of milliseconds of work after an idle
+gap); then exactly K steps bracketed by ``torch.cuda.synchronize()``, whose
+wall time gives ``value``; then K more steps with events for the per-kernel
+breakdown.  Prints ONE JSON line on stdout.
 
 Throughput uses the algorithmic flop count (what the method must compute; the
 masked half under the causal mask is work it avoids):
@@ -229,6 +233,189 @@ def dropout_leg(dev, calls=20, warmup=5, p_drop=0.1):
             "tflops": round(tf, 2), "bound": "mfma", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
+def flops_of(w):
+    return flops(w)
+
+
+def host_info():
+    """CPU model, BLAS library numpy uses, and the host threads the oracle may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version')}".strip()
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "threads": len(os.sched_getaffinity(0))}
+
+
+def sample_sclk():
+    """Current shader clock in MHz as the driver reports it (rocm-smi), or None."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    for card in d.values():
+        if isinstance(card, dict):
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    txt = str(val).lower().replace("(", " ").replace(")", " ").replace("mhz", " ")
+                    for tok in txt.split():
+                        try:
+                            return float(tok)
+                        except ValueError:
+                            continue
+    return None
+
+
+class Layer:
+    """Device buffers of one workload and its step: fa_fwd, fa_bwd_dq, fa_bwd_dkdv."""
+
+    def __init__(self, w, dev):
+        import numpy as np
+        import torch
+        from tiled_attention_14_amd import fa, synth
+        self.w, self.fa = w, fa
+        inp = synth.make_inputs(w)
+        self.inp = inp
+
+        def up(name):
+            if inp.bits is not None:
+                return torch.from_numpy(inp.bits[name].view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(inp.vals[name]).to(dev)
+
+        self.q, self.k, self.v, self.do = up("q"), up("k"), up("v"), up("do")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+        self.ws_buf, self.ws, self.ws_n = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, self.dt, dev)
+        self.stream = torch.cuda.current_stream()
+        self.sargs = (w.B, w.H, w.Hkv, w.N, w.d)
+
+    def step(self, ev=None):
+        fa, w, s = self.fa, self.w, self.stream
+        if ev is not None: ev[0].record(s)
+        st = fa.fa_fwd(self.q, self.k, self.v, self.o, self.lse, *self.sargs, w.scale, w.causal, self.dt, s)
+        if ev is not None: ev[1].record(s)
+        st |= fa.fa_bwd_dq(self.q, self.k, self.v, self.o, self.do, self.lse, self.dq, *self.sargs, w.scale,
+                           w.causal, self.dt, self.ws, self.ws_n, s)
+        if ev is not None: ev[2].record(s)
+        st |= fa.fa_bwd_dkdv(self.q, self.k, self.v, self.do, self.dk, self.dv, *self.sargs, w.scale, w.causal,
+                             self.dt, self.ws, self.ws_n, s)
+        if ev is not None: ev[3].record(s)
+        if st != fa.FA_OK:
+            raise RuntimeError("attention call failed")
+
+    def kernel_times(self, steps):
+        """Average per-kernel milliseconds over `steps` steps (HIP events on the launch stream)."""
+        import numpy as np
+        import torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        names = ["fa_fwd", "fa_bwd_dq", "fa_bwd_dkdv"]
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+
+
+def other_workloads(dev, names, steps=3, warmup=2):
+    """fwd / bwd / fwd+bwd TFLOP/s of the other named workloads (HIP events)."""
+    import torch
+    from tiled_attention_14_amd import synth
+    res = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        L = Layer(w, dev)
+        del L.inp
+        for _ in range(warmup):
+            L.step()
+        per = L.kernel_times(steps)
+        f_fwd, f_bwd, f_tot = flops(w)
+        t_fwd, t_bwd = per["fa_fwd"], per["fa_bwd_dq"] + per["fa_bwd_dkdv"]
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        r = {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d, "dtype": w.dtype,
+             "causal": w.causal, "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+             "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+             "bwd_tflops": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2),
+             "tflops": round(f_tot / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
+             "kernel_ms": {n: round(t, 4) for n, t in per.items()}}
+        r["frac"] = round(r["tflops"] / peak, 4)
+        log(f"[bench] {name}: fwd {t_fwd:.4f} ms ({r['fwd_tflops']} TFLOP/s), bwd {t_bwd:.4f} ms "
+            f"({r['bwd_tflops']} TFLOP/s)")
+        res.append(r)
+        del L
+        torch.cuda.empty_cache()
+    return res
+
+
+def preprocess_leg(L, calls=50, warmup=5):
+    """fa_bwd_preprocess alone on the headline shape (bound by HBM): it reads O,
+    dO and LSE and writes -D and lse * log2 e.  fa_bwd forms the same values
+    inside the dQ kernel; the standalone phase is measured for its bandwidth."""
+    import torch
+    fa, w = L.fa, L.w
+
+    def call():
+        if fa.fa_bwd_preprocess(L.o, L.do, L.lse, *L.sargs, L.dt, L.ws, L.ws_n, L.stream) != fa.FA_OK:
+            raise RuntimeError("fa_bwd_preprocess failed")
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(L.stream)
+    for _ in range(calls):
+        call()
+    e1.record(L.stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    el = 2 if w.dtype == "bf16" else 4
+    nbytes = 2 * w.B * w.H * w.N * w.d * el + 3 * 4 * w.B * w.H * w.N
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] preprocess {w.name}: {us:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": w.name, "us": round(us, 2), "bytes": nbytes, "bound": "hbm", "achieved_gbs": round(gbs, 1),
+            "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def clock_leg(L, seconds=2.0):
+    """Shader clock sampled by rocm-smi while the headline step runs back to back."""
+    import threading
+    import torch
+    box = {}
+    t = threading.Thread(target=lambda: box.setdefault("mhz", sample_sclk()))
+    L.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t.start()
+    n = 0
+    while t.is_alive() or time.perf_counter() - t0 < 0.3:
+        for _ in range(20):
+            L.step()
+        torch.cuda.synchronize()
+        n += 20
+        if time.perf_counter() - t0 > seconds + 20:
+            break
+    t.join(timeout=30)
+    log(f"[bench] shader clock under load: {box.get('mhz')} MHz ({n} steps while sampling)")
+    return box.get("mhz")
+
+
 def main():
     from tiled_attention_14_amd import synth
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -237,7 +424,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode, fp8 and dropout legs (headline only)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the extra legs (other workloads, decode, fp8, dropout, preprocess, clock)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -248,14 +436,10 @@ def main():
               f"(--gpus {args.gpus}, WORLD_SIZE={world} requested); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    from tiled_attention_14_amd import fa
 
     w = synth.WORKLOADS[args.workload]
-    dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} Hkv={w.Hkv} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
-    inp = synth.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -268,62 +452,36 @@ def main():
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
-    def up(name):
-        if inp.bits is not None:
-            return torch.from_numpy(inp.bits[name].view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(inp.vals[name]).to(dev)
-
-    q, k, v, do = up("q"), up("k"), up("v"), up("do")
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_buf, ws, ws_n = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, dt, dev)
-    stream = torch.cuda.current_stream()
-    sargs = (w.B, w.H, w.Hkv, w.N, w.d)
-
-    def step(ev=None):
-        if ev is not None: ev[0].record(stream)
-        st = fa.fa_fwd(q, k, v, o, lse, *sargs, w.scale, w.causal, dt, stream)
-        if ev is not None: ev[1].record(stream)
-        st |= fa.fa_bwd_preprocess(o, do, lse, *sargs, dt, ws, ws_n, stream)
-        if ev is not None: ev[2].record(stream)
-        st |= fa.fa_bwd_dkdv(q, k, v, do, dk, dv, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
-        if ev is not None: ev[3].record(stream)
-        st |= fa.fa_bwd_dq(q, k, v, do, dq, *sargs, w.scale, w.causal, dt, ws, ws_n, stream)
-        if ev is not None: ev[4].record(stream)
-        if st != fa.FA_OK:
-            raise RuntimeError("attention call failed")
-
+    L = Layer(w, dev)
     for _ in range(args.warmup):
-        step()
+        L.step()
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warm-up steps done")
+
+    # K steps with events between the kernels: they bring the shader clock to
+    # its loaded level before the timed region (their times are logged, not used).
+    settle = L.kernel_times(args.steps)
+    log("[bench] settling pass, kernel averages (ms): " + ", ".join(f"{n}={t:.4f}" for n, t in settle.items()))
 
     # Timed region: exactly K steps, no events (wall clock between synchronizations).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        L.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] {args.steps} timed steps: {wall * 1e3 / args.steps:.3f} ms/step")
 
-    # Per-kernel durations: the same K steps again with events between the kernels,
+    # Per-kernel durations: K more steps with events between the kernels,
     # recorded on the stream the kernels are launched on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    names = ["fa_fwd", "fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq"]
-    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    per = L.kernel_times(args.steps)
     log("[bench] kernel averages (ms): " + ", ".join(f"{n}={t:.4f}" for n, t in per.items()))
 
     f_fwd, f_bwd, f_tot = flops(w)
     ms = wall * 1e3 / args.steps
     value = f_tot / (ms * 1e-3) / 1e12
     t_fwd = per["fa_fwd"]
-    t_bwd = per["fa_bwd_pre"] + per["fa_bwd_dkdv"] + per["fa_bwd_dq"]
+    t_bwd = per["fa_bwd_dq"] + per["fa_bwd_dkdv"]
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
 
     # Algorithmic flops per kernel, in units of one N x N x d product (F_fwd / 2):
@@ -337,9 +495,6 @@ def main():
     achieved = algo[dom] / (per[dom] * 1e-3) / 1e12
     traffic = traffic_for_current_kernel(dom) if w.name == synth.HEADLINE else None
 
-    # The preprocess is bound by HBM: it reads O, dO and LSE and writes D and LSE*log2(e).
-    el = 2 if w.dtype == "bf16" else 4
-    pre_bytes = 2 * w.B * w.H * w.N * w.d * el + 3 * 4 * w.B * w.H * w.N
     out = {
         "metric": "attention fwd+bwd TFLOP/s (bf16, causal) and % of MFMA bf16 peak",
         "value": round(value, 2),
@@ -362,16 +517,33 @@ def main():
         "bwd_ms": round(t_bwd, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
         "kernel_mfma_tflops_executed": {n: round(f / (per[n] * 1e-3) / 1e12, 2) for n, f in executed.items()},
-        "bwd_preprocess_gbs": round(pre_bytes / (per["fa_bwd_pre"] * 1e-3) / 1e9, 1),
+        "timing": "W warm-up steps; K steps with events (settling, not used); K wall-timed steps (value); "
+                  "K steps with events (kernel_ms)",
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }
-    out["decode"] = None if args.no_decode else decode_leg(dev)
-    out["fp8_forward"] = None if args.no_decode else fp8_leg(dev)
-    out["dropout"] = None if args.no_decode else dropout_leg(dev)
+    if not args.no_decode:
+        out["sclk_mhz_under_load"] = clock_leg(L)
+        out["bwd_preprocess"] = preprocess_leg(L)
+        others = [n for n in ("mha_bf16_n2048_d64", "llama2_70b_gqa_causal_n8192_d128", "long_seq_causal_n65536_d128")
+                  if n != w.name]
+        inp = L.inp
+        del L
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads(dev, others)
+        out["decode"] = decode_leg(dev)
+        out["fp8_forward"] = fp8_leg(dev)
+        out["dropout"] = dropout_leg(dev)
+    else:
+        inp = L.inp
+        for key in ("sclk_mhz_under_load", "bwd_preprocess", "other_workloads", "decode", "fp8_forward", "dropout"):
+            out[key] = None
+    out["host"] = host_info()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp)
+        out["cpu_baseline"]["cpu_model"] = out["host"]["cpu_model"]
+        out["cpu_baseline"]["blas"] = out["host"]["blas"]
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

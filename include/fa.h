@@ -155,18 +155,21 @@ fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v,
                            float scale, int causal, fa_dtype_t dtype, hipStream_t stream);
 
 /*
- * The three phases of fa_bwd, callable one by one (same arguments, layouts,
- * workspace and error rules as fa_bwd); enqueued on one stream as
- * preprocess, then dkdv and dq (in either order) they do exactly what fa_bwd
- * does.  They exist so that callers and benchmarks can time or schedule the
- * phases separately.
+ * The phases of fa_bwd, callable one by one (same arguments, layouts,
+ * workspace and error rules as fa_bwd).  fa_bwd is fa_bwd_dq followed by
+ * fa_bwd_dkdv on its stream; these exist so that callers and benchmarks can
+ * time or schedule the phases separately.
  *
  * fa_bwd_preprocess: -D_i = -sum_c dO_ic * O_ic and lse_i * log2 e into the
  *   workspace.  Reads o, dO and lse.
- * fa_bwd_dkdv: recomputes P = exp(scale q k^T - lse) and dS = P * (dO v^T - D)
- *   and writes dv = P^T dO and dk = scale dS^T q.  Needs the preprocess.
- * fa_bwd_dq: recomputes P and dS the same way and writes dq = scale dS k.
- *   Needs the preprocess.
+ * fa_bwd_dq: recomputes P = exp(scale q k^T - lse) and dS = P * (dO v^T - D)
+ *   and writes dq = scale dS k.  It forms D and lse * log2 e itself (reading
+ *   o, dO and lse) and writes them to the workspace too, with the same bits
+ *   as fa_bwd_preprocess.
+ * fa_bwd_dkdv: recomputes P and dS the same way and writes dv = P^T dO and
+ *   dk = scale dS^T q.  Reads D and lse * log2 e from the workspace: enqueue
+ *   fa_bwd_dq or fa_bwd_preprocess (same sizes, same workspace) before it.
+ * Any such order gives exactly fa_bwd's results.
  */
 fa_status_t fa_bwd_preprocess(const void* o, const void* dO, const float* lse,
                               int B, int H, int Hkv, int N, int d, fa_dtype_t dtype,
@@ -178,7 +181,8 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         float scale, int causal, fa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
+                      const void* o, const void* dO, const float* lse,
                       void* dq,
                       int B, int H, int Hkv, int N, int d,
                       float scale, int causal, fa_dtype_t dtype,

@@ -80,7 +80,7 @@ def _dkdv(**kw):
 
 def _dq(**kw):
     a = dict(GOOD); a.update(kw)
-    ptrs = a.pop("ptrs", [P] * 5)
+    ptrs = a.pop("ptrs", [P] * 7)
     return fa.fa_bwd_dq(*ptrs, a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
                         a.pop("ws", P), a.pop("wsb", 1 << 40), 0)
 
@@ -136,7 +136,7 @@ def test_phase_invalid_arguments(lib, call, kw, status):
     assert call(**kw) == status
 
 
-@pytest.mark.parametrize("call,n", [(_pre, 3), (_dkdv, 6), (_dq, 5)])
+@pytest.mark.parametrize("call,n", [(_pre, 3), (_dkdv, 6), (_dq, 7)])
 def test_phase_null_and_misaligned_pointers(lib, call, n):
     for i in range(n):
         ptrs = [P] * n

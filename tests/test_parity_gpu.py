@@ -179,9 +179,11 @@ def test_identities_llama2_7b_causal():
 @pytest.mark.parametrize("dt,d,causal,heads", [("bf16", 128, True, (4, 2)), ("bf16", 64, False, (4, 4)),
                                                ("f32", 64, True, (4, 1))])
 def test_phases_equal_fa_bwd(dt, d, causal, heads):
-    """fa_bwd_preprocess then fa_bwd_dq and fa_bwd_dkdv (in that order, the
-    reverse of fa_bwd's) reproduce fa_bwd bit for bit: the backward has no
-    atomics, so its results do not depend on scheduling."""
+    """The phases in any valid order reproduce fa_bwd bit for bit: the
+    backward has no atomics, and fa_bwd_dq writes the same -D and lse * log2 e
+    as fa_bwd_preprocess.  Orders: preprocess, dK/dV, dQ; preprocess, dQ,
+    dK/dV; dQ, dK/dV (fa_bwd's own).  The workspace is filled with garbage
+    before each, so nothing carries over."""
     import torch
     from tiled_attention_14_amd import fa
     H, Hkv = heads
@@ -190,11 +192,16 @@ def test_phases_equal_fa_bwd(dt, d, causal, heads):
     ft = fa.FA_BF16 if dt == "bf16" else fa.FA_F32
     o, lse = fa.forward(t["q"], t["k"], t["v"], w.scale, causal)
     dq, dk, dv = fa.backward(t["q"], t["k"], t["v"], o, t["do"], lse, w.scale, causal)
-    _, ws, n = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, ft, "cuda")
-    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    buf, ws, n = fa.workspace(w.B, w.H, w.Hkv, w.N, w.d, ft, "cuda")
     sh = (w.B, w.H, w.Hkv, w.N, w.d)
-    assert fa.fa_bwd_preprocess(o, t["do"], lse, *sh, ft, ws, n) == fa.FA_OK
-    assert fa.fa_bwd_dq(t["q"], t["k"], t["v"], t["do"], dq2, *sh, w.scale, causal, ft, ws, n) == fa.FA_OK
-    assert fa.fa_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], dk2, dv2, *sh, w.scale, causal, ft, ws, n) == fa.FA_OK
-    torch.cuda.synchronize()
-    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    pre = lambda: fa.fa_bwd_preprocess(o, t["do"], lse, *sh, ft, ws, n)
+    dqf = lambda x: fa.fa_bwd_dq(t["q"], t["k"], t["v"], o, t["do"], lse, x, *sh, w.scale, causal, ft, ws, n)
+    dkdvf = lambda a, b: fa.fa_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], a, b, *sh, w.scale, causal, ft, ws, n)
+    for order in ("pre,dkdv,dq", "pre,dq,dkdv", "dq,dkdv"):
+        buf.fill_(0x7F)
+        dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+        for ph in order.split(","):
+            st = pre() if ph == "pre" else dqf(dq2) if ph == "dq" else dkdvf(dk2, dv2)
+            assert st == fa.FA_OK, (order, ph)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), order

@@ -214,14 +214,14 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
   return fa::launch_bwd_dkdv(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, void* dq, int B, int H, int Hkv,
-                      int N, int d, float scale, int causal, fa_dtype_t dtype, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-  if (!all_aligned({q, k, v, dO, dq})) return FA_ERR_INVALID_ARG;
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                      void* dq, int B, int H, int Hkv, int N, int d, float scale, int causal, fa_dtype_t dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!all_aligned({q, k, v, o, dO, lse, dq})) return FA_ERR_INVALID_ARG;
   fa::BwdParams p;
   fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
-  p.q = q; p.k = k; p.v = v; p.dO = dO; p.dq = dq;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq;
   return fa::launch_bwd_dq(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -233,9 +233,9 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   fa_status_t st = bwd_params(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes, &p);
   if (st != FA_OK) return st;
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
-  if (fa::launch_bwd_pre(p, stream) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
+  // The dQ kernel also writes -D and lse * log2 e, which the dK/dV kernel reads.
   if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -286,9 +286,8 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const vo
   if (st != FA_OK) return st;
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.dq = dq; p.dk = dk; p.dv = dv;
   p.drop = dp;
-  if (fa::launch_bwd_pre(p, stream) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_dq(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dkdv(p, stream) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

@@ -18,7 +18,10 @@
 // Kernels (all on the caller's stream, no host synchronisation):
 //  1. fa_bwd_pre:  -D = -rowsum(dO * O) and lse * log2(e), one float each
 //     per query row, into the workspace (dP - D is then an addition, or the
-//     start value of a dP accumulator);
+//     start value of a dP accumulator).  The dQ kernel (3) computes the same
+//     two values for its own rows, with the same summation order (so the same
+//     bits), and writes them too: fa_bwd runs dQ first and dK/dV second, and
+//     needs no separate preprocessing launch;
 //  2. fa_bwd_dkdv: one workgroup per (batch, KV head, key tile[, slice of
 //     the GQA group]); K/V fragments and the dK/dV accumulators stay in
 //     registers while Q/dO tiles stream through LDS (global -> LDS copies),
@@ -29,9 +32,9 @@
 //     a GQA group is sliced over several workgroups (to balance the work of
 //     very wide groups), each writes float32 partial sums and fa_bwd_reduce
 //     adds them in a fixed order;
-//  3. fa_bwd_dq:   one workgroup per (batch, head, 128-query tile); Q/dO
-//     fragments and the dQ accumulator stay in registers while K/V tiles of 64
-//     keys stream through LDS.  It recomputes S and dP instead of exchanging
+//  3. fa_bwd_dq:   one workgroup per (batch, head, 256-query tile; 128 for
+//     fp32); Q/dO fragments and the dQ accumulator stay in registers while
+//     K/V tiles of 64 keys stream through LDS.  It recomputes S and dP instead of exchanging
 //     dS with the dK/dV kernel: seven products in total instead of five, but
 //     no float atomics, whose L2 throughput on this part is far below what a
 //     shared dQ accumulator would need.
@@ -48,7 +51,8 @@ constexpr int kThreads = 64 * kWaves;
 
 struct BwdArgs {
   const void* q; const void* k; const void* v; const void* dO;
-  const float* delta; const float* lse2;
+  const void* o; const float* lse;
+  float* delta; float* lse2;
   void* dq; void* dk; void* dv;
   float* part;
   int B, H, Hkv, N, nsplit;
@@ -60,6 +64,7 @@ struct BwdArgs {
 BwdArgs make_args(const BwdParams& p) {
   BwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.dO = p.dO;
+  a.o = p.o; a.lse = p.lse;
   a.delta = p.delta; a.lse2 = p.lse2;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.part = p.part;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N; a.nsplit = p.nsplit;
@@ -70,35 +75,55 @@ BwdArgs make_args(const BwdParams& p) {
 }
 
 // ------------------------------------------------------------------ 1. preprocess
-// D/8 threads share a row; each handles 8 elements.
+// D_i = sum_c dO_ic O_ic in one fixed order, shared with the dQ kernel so
+// that both give the same bits.  Row i is cut into chunks of 8 columns,
+// chunk c = 2 s + hf holding columns 8 c .. 8 c + 7 (the columns a lane holds
+// as its k16 fragment s in lane half hf).  Each chunk is summed with fused
+// multiply-adds in column order; the chunks of one half (fixed hf) are added
+// as a pairwise tree over s (s with s ^ 1, then ^ 2, then ^ 4); the two halves
+// are added last.
+template <typename T>
+__device__ __forceinline__ float chunk_dot(const typename Frag<T>::type& o, const typename Frag<T>::type& g) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+  return acc;
+}
+// Pairwise tree over the KS chunk sums of one half, in the order above.
+template <int KS>
+__device__ __forceinline__ float chunk_tree(float (&c)[KS]) {
+#pragma unroll
+  for (int m = 1; m < KS; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < KS; i += 2 * m) c[i] = c[i] + c[i + m];
+  return c[0];
+}
+
+// D/8 threads per row, one chunk each (coalesced 16-byte loads for bf16).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                          const float* __restrict__ lse, float* __restrict__ delta,
                                                          float* __restrict__ lse2, long rows) {
-  constexpr int TPR = D / 8;
+  typedef typename Frag<T>::type F;
+  constexpr int CPR = D / 8;  // chunks per row
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = t / TPR;
-  const int c8 = (int)(t % TPR);
-  float acc = 0.f;
+  const long row = t / CPR;
+  const int c = (int)(t % CPR);
+  float v = 0.f;
   if (row < rows) {
-    const size_t off = (size_t)row * D + c8 * 8;
-    float o[8], g[8];
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(O + off);
-      const bf16x8 y = *reinterpret_cast<const bf16x8*>(dO + off);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { o[i] = (float)x[i]; g[i] = (float)y[i]; }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { o[i] = O[off + i]; g[i] = dO[off + i]; }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(o[i], g[i], acc);
+    const rsrc_t rO = make_rsrc(O + row * D, (uint32_t)(D * sizeof(T)));
+    const rsrc_t rG = make_rsrc(dO + row * D, (uint32_t)(D * sizeof(T)));
+    F o, g;
+    frag_global<D>(o, rO, 0, 8 * c);
+    frag_global<D>(g, rG, 0, 8 * c);
+    v = chunk_dot<T>(o, g);
   }
+  // chunk c = 2 s + hf: the tree over s pairs lanes c ^ 2, c ^ 4, c ^ 8; then the halves (c ^ 1).
 #pragma unroll
-  for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, TPR);
-  if (row < rows && c8 == 0) {
-    delta[row] = -acc;
+  for (int m = 2; m < CPR; m <<= 1) v = v + __shfl_xor(v, m, CPR);
+  v = v + __shfl_xor(v, 1, CPR);
+  if (row < rows && c == 0) {
+    delta[row] = -v;
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -824,16 +849,32 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   F qf[KS], of[KS];
   float l2, dd;
   {
+    // Q and dO rows of this lane, and the backward preprocessing of its row
+    // (-D and lse * log2 e, also written for the dK/dV kernel): D from the O
+    // and dO fragments in the order of fa_bwd_pre_kernel (fragment s of lane
+    // half hf is chunk 2 s + hf there).
     const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)bh * slab, slab_bytes);
-    const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)bh * slab, slab_bytes);
+    const rsrc_t rG = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)bh * slab, slab_bytes);
+    const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.o) + (size_t)bh * slab, slab_bytes);
+    F ofw[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
-      frag_global<D>(of[s], rO, myq, 16 * s + 8 * hf);
+      frag_global<D>(of[s], rG, myq, 16 * s + 8 * hf);
+      frag_global<D>(ofw[s], rO, myq, 16 * s + 8 * hf);
     }
-    l2 = load4f(make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
-    dd = load4f(make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
+    const float lse = load4f(make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
     wait_loads();
+    float cs[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) cs[s2] = chunk_dot<T>(ofw[s2], of[s2]);
+    const float part = chunk_tree<KS>(cs);
+    dd = -(part + other_half(part));
+    l2 = lse * kLog2e;
+    if (hf == 0 && myq < N) {
+      a.delta[(size_t)bh * N + myq] = dd;
+      a.lse2[(size_t)bh * N + myq] = l2;
+    }
   }
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kQTile) : N;

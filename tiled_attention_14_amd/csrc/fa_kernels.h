@@ -82,9 +82,10 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Params& p, hipStream_t stream);
 hipError_t launch_fwd_split(const SplitParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
-// Backward phases, in stream order: preprocess (D and lse2), then the dK/dV
-// kernel (plus the reduction of its partials when nsplit > 1) and the dQ
-// kernel, which are independent of each other.
+// Backward phases: preprocess (D and lse2 into the workspace), the dQ kernel
+// (which writes the same D and lse2 for its rows before using them) and the
+// dK/dV kernel (plus the reduction of its partials when nsplit > 1), which
+// reads them: preprocess or dQ must come before dK/dV on the stream.
 hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);

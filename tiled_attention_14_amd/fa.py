@@ -49,7 +49,7 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_preprocess.restype = I
         L.fa_bwd_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         L.fa_bwd_dkdv.restype = I
-        L.fa_bwd_dq.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        L.fa_bwd_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         L.fa_bwd_dq.restype = I
         L.fa_fwd_splitkv_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         L.fa_fwd_splitkv_workspace_size.restype = S
@@ -145,9 +145,9 @@ def fa_bwd_dkdv(q, k, v, dO, dk, dv, B, H, Hkv, N, d, scale, causal, dtype,
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
-def fa_bwd_dq(q, k, v, dO, dq, B, H, Hkv, N, d, scale, causal, dtype,
+def fa_bwd_dq(q, k, v, o, dO, lse, dq, B, H, Hkv, N, d, scale, causal, dtype,
               workspace, workspace_bytes, stream=None) -> int:
-    return lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq),
+    return lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                            B, H, Hkv, N, d, float(scale), int(bool(causal)), int(dtype),
                            _ptr(workspace), int(workspace_bytes), _stream(stream))
 
