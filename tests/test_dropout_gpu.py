@@ -76,6 +76,60 @@ def test_mask_bit_exact(dt, d, N, causal):
     assert not np.any(got["o"][..., N:])
 
 
+@pytest.mark.parametrize("which", ["dk", "dq"])
+@pytest.mark.parametrize("dt,d,N,causal", [("bf16", 128, 128, True), ("bf16", 64, 61, False),
+                                           ("f32", 128, 100, False), ("f32", 64, 64, True)])
+def test_mask_element_by_element_in_dk_and_dq(which, dt, d, N, causal):
+    """The mask as the dS wave of the dK/dV kernel and the dQ kernel apply it.
+    With Q = one-hot rows (Q[i] = e_i), dK[j, i] = scale * dS[i, j]; with K =
+    one-hot rows, dQ[i, j] = scale * dS[i, j]: every element of the checked
+    gradient is one element of dS = P (dP M / keep - D).  Each must match the
+    oracle's (correct-mask) value within a rounding bound, and flipping the
+    mask bit of an element would move its value by P dP / keep, which is
+    required to exceed twice that bound for most visible elements, so a
+    single misplaced mask bit fails the test."""
+    import torch
+    B, H, p, seed, off = 1, 2, 0.3, 0xBADC0FFEE, 5
+    w = synth.Workload("mask_dkdq", B, H, H, N, d, dt, causal, seed=9300 + N + d)
+    inp = synth.make_inputs(w)
+    onehot = np.zeros((B, H, N, d), dtype=np.float32)
+    onehot[:, :, np.arange(N), np.arange(N)] = 1.0
+    vals = dict(inp.vals)
+    vals["q" if which == "dk" else "k"] = onehot
+    bits = None if inp.bits is None else {n: synth.bf16_round_bits(x) for n, x in vals.items()}
+    inp = synth.Inputs(w, vals, bits)
+    _, got = _run(w, p, seed, off, to_device(inp))
+    ref, _ = _refs(w, inp, p, seed, off)
+    g, r = got[which][..., :N], ref[which][..., :N]
+    if which == "dk":  # dK[j, i] = scale dS[i, j]: put both in (i, j) order
+        g, r = np.swapaxes(g, -1, -2), np.swapaxes(r, -1, -2)
+    # Size of the change a flipped mask bit would cause: scale P dP / keep.
+    q, k, v, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    S = w.scale * q @ np.swapaxes(k, -1, -2)
+    vis = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    S = np.where(vis, S, -np.inf)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    keep = 1.0 - round(256 * p) / 256
+    flip = np.abs(w.scale * P * (do @ np.swapaxes(v, -1, -2)) / keep)
+    scale_ref = float(np.max(np.abs(r)))
+    # Rounding bound per element: dS and the output rounded to bf16 (or fp32
+    # noise), plus the absolute error of dP M / keep - D, which matters where
+    # the two terms cancel: D = rowsum(dO * O) formed from the stored (bf16) O,
+    # and dP accumulated in fp32 over d products.
+    u_o = 2.0 ** -8 if dt == "bf16" else 2.0 ** -23
+    dD = u_o * np.sum(np.abs(do * ref["o"]), axis=-1, keepdims=True)
+    dDP = 2.0 ** -16 * (np.abs(do) @ np.swapaxes(np.abs(v), -1, -2)) / keep
+    tol = w.scale * P * (dD + dDP) + ((1e-2 * np.abs(r) + 1e-5 * scale_ref) if dt == "bf16"
+                                      else (1e-5 * np.abs(r) + 1e-7 * scale_ref))
+    err = np.abs(g - r)
+    sensitive = vis & (flip > 2 * tol)
+    say(f"[dropout]   {which}: max err/tol {float(np.max(np.where(vis, err / tol, 0))):.3f}, "
+        f"elements where a flipped bit would show: {sensitive.sum()} of {vis.sum() * B * H} visible")
+    assert np.all(err <= tol), f"{which}: {int((err > tol).sum())} elements off the correct-mask value"
+    assert sensitive.sum() >= 0.8 * vis.sum() * B * H
+
+
 SWEEP = [
     # dtype, d, causal, B, H, Hkv, N, p, seed, offset
     ("bf16", 128, True, 1, 4, 2, 300, 0.1, 1, 0),
