@@ -248,7 +248,9 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v,
  * enough workgroups to fill the GPU), each processed by its own workgroups,
  * which write float32 partial results (O over the range, normalised over the
  * range, and the range's log-sum-exp) into `workspace`; fa_merge then
- * combines them into o and lse on the same stream.  The partials are the
+ * combines them into o and lse on the same stream.  When the sizes give a
+ * single range, its workgroups write o and lse directly (the values the
+ * merge would produce) and no merge runs.  The partials are the
  * per-block results of the incremental softmax of "FlashAttention 在昇腾NPU上到底
  * 快在哪", section 三、增量 Softmax, the merge its correction step, here across
  * workgroups: short query blocks (the cache reuse of section 七 of the same

@@ -315,11 +315,13 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   p.q = q; p.k = k; p.v = v;
   p.opart = static_cast<float*>(workspace);
   p.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+  p.o = o; p.lse = lse;
   p.B = B; p.H = H; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d;
   p.nsplit = count; p.split_len = len;
   p.scale = scale; p.causal = causal != 0;
   p.dtype = dtype == FA_BF16 ? fa::kBF16 : fa::kF32;
   if (fa::launch_fwd_split(p, stream) != hipSuccess) return FA_ERR_HIP;
+  if (count == 1) return FA_OK;  // the single range wrote o and lse itself
   fa::MergeParams mp;
   mp.opart = p.opart; mp.lpart = p.lpart; mp.o = o; mp.lse = lse;
   mp.rows = (long)B * H * Nq; mp.nsplit = count; mp.d = d; mp.dtype = p.dtype;

@@ -53,6 +53,7 @@ struct BwdParams {
 struct SplitParams {
   const void* q; const void* k; const void* v;
   float* opart; float* lpart;
+  void* o; float* lse;  // final outputs, written directly when nsplit == 1
   int B, H, Hkv, Nq, Nk, d;
   int nsplit, split_len;
   float scale;

@@ -23,6 +23,8 @@
 //    K Q^T on bf16 MFMA, P V in fp16 for bf16 inputs);
 //  * each range writes float32 O and LSE per row; a row that sees no key of
 //    the range writes O = 0 and LSE = -inf, which the merge weights by 0.
+//    With a single range the kernel writes the final O (in the input dtype)
+//    and LSE itself, the values the merge would produce, and no merge runs.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -38,6 +40,7 @@ constexpr float kSplitSlack = 8.f;            // log2 units the running max may 
 struct SplitArgs {
   const void* q; const void* k; const void* v;
   float* opart; float* lpart;
+  void* o; float* lse;  // nsplit == 1: the range is the whole row, written here directly
   int B, H, Hkv, Nq, Nk;
   int nrb;        // row blocks per (batch, KV head)
   int nsplit;     // key ranges
@@ -230,8 +233,15 @@ __global__ __launch_bounds__(kSplitThreads, sizeof(T) == 2 ? 2 : 1) void fa_fwd_
 
   lsum += other_half(lsum);
   const bool seen = lsum > 0.f;
-  store_rows<float, D>(a.opart, (int)pidx, rvalid ? (int)pidx + 1 : (int)pidx, acc, seen ? 1.f / lsum : 0.f);
-  if (rvalid && hf == 0) a.lpart[pidx] = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  const float inv = seen ? 1.f / lsum : 0.f;
+  const float lse = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (a.nsplit == 1) {
+    store_rows<T, D>(reinterpret_cast<T*>(a.o), (int)orow, rvalid ? (int)orow + 1 : (int)orow, acc, inv);
+    if (rvalid && hf == 0) a.lse[orow] = lse;
+  } else {
+    store_rows<float, D>(a.opart, (int)pidx, rvalid ? (int)pidx + 1 : (int)pidx, acc, inv);
+    if (rvalid && hf == 0) a.lpart[pidx] = lse;
+  }
 }
 
 // Variant for bf16 with at most 32 rows per KV head (decoding: g heads x a
@@ -388,8 +398,15 @@ __global__ __launch_bounds__(kSplitThreads, 2) void fa_fwd_split_ring_kernel(Spl
   if (w != 0) return;
   lsum += other_half(lsum);
   const bool seen = lsum > 0.f;
-  store_rows<float, D>(a.opart, (int)pidx, rvalid ? (int)pidx + 1 : (int)pidx, acc, seen ? 1.f / lsum : 0.f);
-  if (rvalid && hf == 0) a.lpart[pidx] = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  const float inv = seen ? 1.f / lsum : 0.f;
+  const float lse = seen ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  if (a.nsplit == 1) {
+    store_rows<T, D>(reinterpret_cast<T*>(a.o), (int)orow, rvalid ? (int)orow + 1 : (int)orow, acc, inv);
+    if (rvalid && hf == 0) a.lse[orow] = lse;
+  } else {
+    store_rows<float, D>(a.opart, (int)pidx, rvalid ? (int)pidx + 1 : (int)pidx, acc, inv);
+    if (rvalid && hf == 0) a.lpart[pidx] = lse;
+  }
 }
 
 // Merge of the ranges: one thread per 4 columns of one row.  LSE = log sum
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_split_t(const SplitParams& p, hipStream_t stream) {
   SplitArgs a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.opart = p.opart; a.lpart = p.lpart;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.opart = p.opart; a.lpart = p.lpart; a.o = p.o; a.lse = p.lse;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.Nq = p.Nq; a.Nk = p.Nk;
   a.nrb = (p.H / p.Hkv * p.Nq + kSplitRows - 1) / kSplitRows;
   a.nsplit = p.nsplit;
