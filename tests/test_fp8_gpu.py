@@ -21,9 +21,9 @@ pytestmark = pytest.mark.gpu
 U8, U = 2.0 ** -4, 2.0 ** -8
 
 
-def _run(B, H, Hkv, N, causal, seed):
+def _run(B, H, Hkv, N, causal, seed, qk_std=1.0):
     import torch
-    inp = synth.make_fp8_inputs(B, H, Hkv, N, 128, seed)
+    inp = synth.make_fp8_inputs(B, H, Hkv, N, 128, seed, qk_std=qk_std)
     t = {n: torch.from_numpy(inp.codes[n]).to("cuda") for n in ("q", "k", "v")}
     o = torch.empty((B, H, N, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -63,8 +63,23 @@ def test_fp8_small(B, H, Hkv, N, causal):
     _check(inp, scale, causal, o, lse)
 
 
-def test_fp8_llama2_7b_shape_sampled_rows():
+def test_fp8_llama2_7b_shape_every_row():
     B, H, N = 2, 32, 4096
     inp, scale, o, lse = _run(B, H, H, N, True, seed=8100)
-    rows = synth.sample_rows(N, 256, 8101, B * H).reshape(B, H, -1)
+    _check(inp, scale, True, o, lse)
+
+
+def test_fp8_llama2_70b_gqa_shape_sampled_rows():
+    B, H, Hkv, N = 1, 64, 8, 8192
+    inp, scale, o, lse = _run(B, H, Hkv, N, True, seed=8200)
+    rows = synth.sample_rows(N, 256, 8201, B * H).reshape(B, H, -1)
+    _check(inp, scale, True, o, lse, rows=rows)
+
+
+def test_fp8_long_sequence_sampled_rows():
+    # The long-sequence distribution (Q and K with std 2: peaked rows) over
+    # 65536 keys, where the running max moves most.
+    B, H, N = 1, 8, 65536
+    inp, scale, o, lse = _run(B, H, H, N, True, seed=8300, qk_std=2.0)
+    rows = synth.sample_rows(N, 256, 8301, B * H).reshape(B, H, -1)
     _check(inp, scale, True, o, lse, rows=rows)
