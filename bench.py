@@ -50,6 +50,17 @@ def flops(w):
     return f_fwd, 2.5 * f_fwd, 3.5 * f_fwd
 
 
+def hbm_bytes(w):
+    """Algorithmic HBM bytes of one fwd + bwd pass: every input read once and
+    every output written once (forward: Q, K, V in, O and LSE out; backward:
+    Q, K, V, O, dO, LSE in, dQ, dK, dV out)."""
+    e = 2 if w.dtype == "bf16" else 4
+    q = w.B * w.H * w.N * w.d * e
+    kv = w.B * w.Hkv * w.N * w.d * e
+    rows = w.B * w.H * w.N * 4
+    return (2 * q + 2 * kv + rows) + (4 * q + 4 * kv + rows)
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -356,6 +367,12 @@ def other_workloads(dev, names, steps=3, warmup=2):
              "tflops": round(f_tot / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
              "kernel_ms": {n: round(t, 4) for n, t in per.items()}}
         r["frac"] = round(r["tflops"] / peak, 4)
+        # Intensity of the whole pass: far above the ridge point (peak flop/s
+        # over 8 TB/s, about 313 flop/B for bf16), so even the shortest named
+        # sequence is bound by the matrix cores and the softmax, not by HBM.
+        r["hbm_bytes"] = hbm_bytes(w)
+        r["flop_per_byte"] = round(f_tot / r["hbm_bytes"], 1)
+        r["achieved_gbs"] = round(r["hbm_bytes"] / ((t_fwd + t_bwd) * 1e-3) / 1e9, 1)
         log(f"[bench] {name}: fwd {t_fwd:.4f} ms ({r['fwd_tflops']} TFLOP/s), bwd {t_bwd:.4f} ms "
             f"({r['bwd_tflops']} TFLOP/s)")
         res.append(r)
