@@ -32,8 +32,8 @@
 //     a GQA group is sliced over several workgroups (to balance the work of
 //     very wide groups), each writes float32 partial sums and fa_bwd_reduce
 //     adds them in a fixed order;
-//  3. fa_bwd_dq:   one workgroup per (batch, head, 256-query tile; 128 for
-//     fp32); Q/dO fragments and the dQ accumulator stay in registers while
+//  3. fa_bwd_dq:   one workgroup per (batch, head, query tile: 256 rows for
+//     bf16 at d = 128, 128 for bf16 at d = 64 and for fp32); Q/dO fragments and the dQ accumulator stay in registers while
 //     K/V tiles of 64 keys stream through LDS.  It recomputes S and dP instead of exchanging
 //     dS with the dK/dV kernel: seven products in total instead of five, but
 //     no float atomics, whose L2 throughput on this part is far below what a
@@ -820,9 +820,12 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ 3. dQ
-// Waves (32 query rows each) per dQ workgroup: bf16 eight, two per SIMD, so
-// that each K/V tile copy serves 256 query rows; fp32 kWaves.
-constexpr int kDqWavesBf16 = 8;
+// Waves (32 query rows each) per dQ workgroup: bf16 at d = 128 eight, two per
+// SIMD, so that each K/V tile copy serves 256 query rows; bf16 at d = 64 four,
+// with three workgroups per CU (at most 168 registers per wave), so that three
+// waves share each SIMD; fp32 kWaves.
+template <int D> constexpr int dq_waves_bf16() { return D == 64 ? 4 : 8; }
+template <int D> constexpr int dq_wgs_bf16() { return D == 64 ? 3 : 2; }
 constexpr int kKTile = 64;           // keys per streamed tile
 
 template <typename T, int D, bool CAUSAL, int NW, bool DROP>
@@ -983,8 +986,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
 }
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(64 * kDqWavesBf16, DROP ? 1 : 2) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
-  dq_body<bf16, D, CAUSAL, kDqWavesBf16, DROP>(a, nqt);
+__global__ __launch_bounds__(64 * dq_waves_bf16<D>(), DROP ? 1 : dq_wgs_bf16<D>()) void fa_bwd_dq_kernel_bf16(BwdArgs a, int nqt) {
+  dq_body<bf16, D, CAUSAL, dq_waves_bf16<D>(), DROP>(a, nqt);
 }
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel_f32(BwdArgs a, int nqt) {
@@ -1025,14 +1028,14 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
   const BwdArgs a = make_args(p);
-  const int qtile = 32 * (sizeof(T) == 2 ? kDqWavesBf16 : kWaves);
+  const int qtile = 32 * (sizeof(T) == 2 ? dq_waves_bf16<D>() : kWaves);
   const int nqt = (p.N + qtile - 1) / qtile;
   const dim3 grid((unsigned)((long)nqt * p.B * p.H));
   if constexpr (sizeof(T) == 2) {
     if (p.drop.on)
-      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, true>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
+      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, true>), grid, dim3(64 * dq_waves_bf16<D>()), 0, stream, a, nqt);
     else
-      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, false>), grid, dim3(64 * kDqWavesBf16), 0, stream, a, nqt);
+      hipLaunchKernelGGL((fa_bwd_dq_kernel_bf16<D, CAUSAL, false>), grid, dim3(64 * dq_waves_bf16<D>()), 0, stream, a, nqt);
   } else {
     if (p.drop.on) hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL, true>), grid, dim3(kThreads), 0, stream, a, nqt);
     else hipLaunchKernelGGL((fa_bwd_dq_kernel_f32<D, CAUSAL, false>), grid, dim3(kThreads), 0, stream, a, nqt);

@@ -12,9 +12,9 @@
 // 改进2：并行化策略优化).
 //
 // Mapping onto the CDNA4 compute unit:
-//  * one workgroup = 8 wavefronts = 256 query rows (bf16; 4 and 128 for
-//    fp32); each wave owns 32 rows, whose Q fragments stay in registers for
-//    the whole kernel;
+//  * one workgroup = 8 wavefronts = 256 query rows (bf16 at d = 128; 4 and
+//    128 for bf16 at d = 64 and for fp32); each wave owns 32 rows, whose Q
+//    fragments stay in registers for the whole kernel;
 //  * K/V tiles of 64 keys go global -> LDS directly (buffer loads with the LDS
 //    destination), double-buffered: the copies of tile j+1 are in flight while
 //    tile j is consumed; rows past N arrive as zeros;
@@ -48,10 +48,14 @@
 namespace fa {
 namespace {
 
-// Waves per workgroup (32 query rows each).  bf16: eight waves, two per
-// SIMD, share each K/V tile, its copy and the V conversion (one workgroup per
-// CU by LDS); fp32 (more registers per wave): four.
-constexpr int kWavesBf16 = 8;
+// Waves per workgroup (32 query rows each).  bf16, d = 128: eight waves, two
+// per SIMD, share each K/V tile, its copy and the V conversion (one workgroup
+// per CU by registers).  bf16, d = 64: four waves, and the register bound asks
+// for three workgroups per CU (at most 168 registers per wave), so three waves
+// from different workgroups share each SIMD.  fp32 (more registers per wave):
+// four.
+template <int D> constexpr int waves_bf16() { return D == 64 ? 4 : 8; }
+template <int D> constexpr int wgs_bf16() { return D == 64 ? 3 : 2; }
 constexpr int kWavesF32 = 4;
 constexpr int kBc = 64;           // keys per tile
 constexpr float kSlack = 8.f;     // log2 units the running max may lag behind
@@ -318,11 +322,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 }
 
 // With dropout the generator's registers come on top of the tile's: those
-// variants ask for one wave per SIMD at least (the second bound), which lets
-// the compiler go past 256 registers if it chooses to.
+// variants ask for one workgroup per CU only (the second bound).  At d = 64
+// (four waves) that is one wave per SIMD, so the compiler may use up to 512
+// registers; at d = 128 the eight waves of a workgroup are two per SIMD, and
+// 256 stays the limit.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(64 * kWavesBf16, DROP ? 1 : 2) void fa_fwd_kernel_bf16(FwdArgs a) {
-  fwd_body<bf16, D, CAUSAL, kWavesBf16, DROP>(a);
+__global__ __launch_bounds__(64 * waves_bf16<D>(), DROP ? 1 : wgs_bf16<D>()) void fa_fwd_kernel_bf16(FwdArgs a) {
+  fwd_body<bf16, D, CAUSAL, waves_bf16<D>(), DROP>(a);
 }
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(64 * kWavesF32, 1) void fa_fwd_kernel_f32(FwdArgs a) {
@@ -334,7 +340,7 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.N = p.N;
-  constexpr int waves = sizeof(T) == 2 ? kWavesBf16 : kWavesF32;
+  constexpr int waves = sizeof(T) == 2 ? waves_bf16<D>() : kWavesF32;
   a.nqt = (p.N + 32 * waves - 1) / (32 * waves);
   a.c = p.scale * kLog2e;
   a.drop = DropArgs{p.drop.k0, p.drop.k1, p.drop.offset, p.drop.t, p.drop.inv};
