@@ -271,7 +271,7 @@ def host_info():
 
 
 def sample_sclk():
-    """Current shader clock in MHz as the driver reports it (rocm-smi), or None."""
+    """Current shader clock in MHz as rocm-smi reports it, or None."""
     import shutil
     import subprocess
     exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
