@@ -116,6 +116,7 @@ def _canary_intact(buf, name):
 @pytest.mark.parametrize("dt,d,causal,N,heads", [
     ("bf16", 128, True, 777, (2, 4, 2)),    # sliced GQA group: float32 partials in the workspace
     ("bf16", 64, False, 1000, (1, 8, 1)),
+    ("bf16", 64, True, 333, (1, 4, 2)),     # four-wave workgroups at d = 64, ragged causal tail
     ("bf16", 128, False, 129, (1, 3, 3)),
     ("f32", 128, True, 300, (1, 4, 2)),
     ("f32", 64, False, 97, (2, 2, 1)),
