@@ -170,6 +170,34 @@ def test_workload_long_seq_causal():
     _identities(w, inp, full)
 
 
+def test_longest_sequence_sampled():
+    """The longest sequence tried: N = 2^20 + 37 (ragged), two query heads on
+    one KV head, causal, bf16.  64 sampled query rows (O, LSE, dQ) and 64
+    sampled key rows among the last 512 (dK, dV: under the causal mask only the
+    queries at or after a key see it, which keeps the oracle's work small while
+    testing the largest offsets), the exact identities and a NaN/Inf scan on
+    the full tensors."""
+    import torch
+    w = synth.Workload("longest_causal_n1048613_d128", 1, 2, 1, (1 << 20) + 37, 128, "bf16", True, seed=14200)
+    inp = synth.make_inputs(w)
+    say(f"[parity] {w.name}: running GPU fwd+bwd")
+    g = run_gpu(w, to_device(inp))
+    rows = synth.sample_rows(w.N, 64, w.seed + 1, w.B * w.H).reshape(w.B, w.H, -1)
+    krows = (w.N - 512 + synth.sample_rows(512, 64, w.seed + 2, w.B * w.Hkv)).reshape(w.B, w.Hkv, -1)
+    ri, ki = torch.from_numpy(rows).to("cuda"), torch.from_numpy(krows).to("cuda")
+    take = lambda t, idx: torch.gather(t, 2, idx[..., None].expand(-1, -1, -1, t.shape[-1])) if t.dim() == 4 \
+        else torch.gather(t, 2, idx)
+    gpu = {"o": host64(take(g["o"], ri)), "lse": host64(take(g["lse"], ri)), "dq": host64(take(g["dq"], ri)),
+           "dk": host64(take(g["dk"], ki)), "dv": host64(take(g["dv"], ki))}
+    say(f"[parity] {w.name}: oracle on {rows.shape[-1]} query rows / {krows.shape[-1]} key rows per head")
+    q, k, v, do = inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do")
+    O, LSE = attention_fwd_ref(q, k, v, w.scale, w.causal, rows=rows)
+    dQ, dK, dV = attention_bwd_ref(q, k, v, do, w.scale, w.causal, rows=rows, key_rows=krows)
+    del q, k, v, do
+    check(w, gpu, {"o": O, "lse": LSE, "dq": dQ, "dk": dK, "dv": dV}, "sampled")
+    _identities(w, inp, g)
+
+
 def test_identities_llama2_7b_causal():
     w = synth.WORKLOADS["llama2_7b_causal_n4096_d128"]
     inp = synth.make_inputs(w)
