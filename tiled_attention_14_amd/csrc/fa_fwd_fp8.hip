@@ -128,6 +128,10 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  // The e4m3 P operand.  Each word is rewritten in two halves every tile; the
+  // first conversion takes the word's previous value as the half it keeps, so
+  // no register has to be cleared first.
+  i32x8 pf = {};
 
   auto tile = [&](const char* sK, const char* sV, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -169,7 +173,6 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
     // 2^kPExp p, summed in fp32 and packed to e4m3 in register order (byte
     // 16 kb + i of the operand = register i of key block kb).
     const float mb = m - kPExp;
-    i32x8 pf;
     float ts = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
         const float p2 = fast_exp2(__builtin_fmaf(s[kb][i + 2], a.c, -mb));
         const float p3 = fast_exp2(__builtin_fmaf(s[kb][i + 3], a.c, -mb));
         ts += (p0 + p1) + (p2 + p3);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[(16 * kb + i) >> 2], false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
         pf[(16 * kb + i) >> 2] = wd;
       }
