@@ -487,7 +487,8 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     if (w == kPairWaves - 1) vec_to_lds<kPairRows>(buffer_desc(a.delta + head * N, (uint32_t)N * 4u), sD[buf], qb0);
   };
 
-  // This wave's 64 keys of K (P wave) or V (dS wave) as B fragments.
+  // This wave's 64 keys of K (P wave) or V (dS wave) as B fragments; they
+  // land while the first tiles are copied.
   F kv[2][KS];
   {
     const bf16* src = reinterpret_cast<const bf16*>(w < 4 ? a.k : a.v) + (size_t)bkv * slab;
@@ -496,7 +497,6 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < KS; ++s) frag_global<D>(kv[kb][s], r, kp + 32 * kb + l32, 16 * s + 8 * hf);
-    wait_loads();
   }
   // dV^T (P wave) or dK^T (dS wave) of the pair's two 32-key blocks.
   f32x16 acc[2][DB];
@@ -508,7 +508,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
   // The dS wave's first dK multiplies a zero dS with buffer 3; keep it finite.
   lds_zero<kPairThreads>(sQ[3], TQ);
   if (total > 0) fetch(0, 0);
-  wait_copies();
+  wait_loads();  // the K or V rows and the copies
   __syncthreads();
 
   constexpr int R = kPairAhead + 1;
@@ -849,35 +849,21 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
   const uint32_t slab_bytes = (uint32_t)(slab * sizeof(T));
   const int q0w = qt * kQTile + 32 * w;
   const int myq = q0w + l32;
-  F qf[KS], of[KS];
-  float l2, dd;
+  F qf[KS], of[KS], ofw[KS];
+  float l2, dd, lse;
   {
-    // Q and dO rows of this lane, and the backward preprocessing of its row
-    // (-D and lse * log2 e, also written for the dK/dV kernel): D from the O
-    // and dO fragments in the order of fa_bwd_pre_kernel (fragment s of lane
-    // half hf is chunk 2 s + hf there).
+    // Q, dO and O rows of this lane and its LSE; the row terms are formed
+    // once these and the first K/V tile have arrived.
     const rsrc_t rQ = make_rsrc(reinterpret_cast<const T*>(a.q) + (size_t)bh * slab, slab_bytes);
     const rsrc_t rG = make_rsrc(reinterpret_cast<const T*>(a.dO) + (size_t)bh * slab, slab_bytes);
     const rsrc_t rO = make_rsrc(reinterpret_cast<const T*>(a.o) + (size_t)bh * slab, slab_bytes);
-    F ofw[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
       frag_global<D>(of[s], rG, myq, 16 * s + 8 * hf);
       frag_global<D>(ofw[s], rO, myq, 16 * s + 8 * hf);
     }
-    const float lse = load4f(make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
-    wait_loads();
-    float cs[KS];
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) cs[s2] = chunk_dot<T>(ofw[s2], of[s2]);
-    const float part = chunk_tree<KS>(cs);
-    dd = -(part + other_half(part));
-    l2 = lse * kLog2e;
-    if (hf == 0 && myq < N) {
-      a.delta[(size_t)bh * N + myq] = dd;
-      a.lse2[(size_t)bh * N + myq] = l2;
-    }
+    lse = load4f(make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4u), (uint32_t)myq * 4u);
   }
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kQTile) : N;
@@ -899,7 +885,24 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     tc.issue(Vh, N, k0, sV);
   };
   copy_kv(sK0, sV0, 0);
-  wait_copies();
+  __builtin_amdgcn_sched_barrier(0);  // the row terms after the copies are issued
+  wait_loads();  // the row fragments, the LSE and the copies
+  {
+    // The backward preprocessing of this lane's row (-D and lse * log2 e,
+    // also written for the dK/dV kernel): D from the O and dO fragments in the
+    // order of fa_bwd_pre_kernel (fragment s of lane half hf is chunk 2 s + hf
+    // there).
+    float cs[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) cs[s2] = chunk_dot<T>(ofw[s2], of[s2]);
+    const float part = chunk_tree<KS>(cs);
+    dd = -(part + other_half(part));
+    l2 = lse * kLog2e;
+    if (hf == 0 && myq < N) {
+      a.delta[(size_t)bh * N + myq] = dd;
+      a.lse2[(size_t)bh * N + myq] = l2;
+    }
+  }
   __syncthreads();
 
   f32x16 acc[DB];

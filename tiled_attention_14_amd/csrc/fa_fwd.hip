@@ -106,10 +106,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   const int q0w = qt * kBr + 32 * w;  // first query row of this wave
   const int myq = q0w + l32;          // query row owned by this lane
+  // Q rows; they land while the tiles are cleared and the first one copied.
   F qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) frag_global<D>(qf[s], rQ, myq, 16 * s + 8 * hf);
-  wait_loads();
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBr) : N;
   const int nt = (kend + kBc - 1) / kBc;
@@ -139,7 +139,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if constexpr (kConv) tc.store_f16(vr, sV);
   };
   copy_kv(sK0, sV0, 0);
-  wait_copies();
+  wait_loads();  // the Q rows, V's registers and the copies
   finish_v(sV0);
   __syncthreads();
 

@@ -88,7 +88,6 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
       const u32x4 hi = load16(rQ, (uint32_t)(myq * kD8 + 64 * s + 32 + 16 * hf));
       qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    wait_loads();
   }
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBr8) : N;
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   lds_zero<64 * kW8>(sV0, TBK); lds_zero<64 * kW8>(sV1, TBK);
   __syncthreads();
   copy_kv(sK0, sV0, 0);
-  wait_copies();
+  wait_loads();  // the Q rows and the copies
   __syncthreads();
 
   float m = -INFINITY, lsum = 0.f;
