@@ -784,15 +784,19 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     dk(sQ[(total - 1) & 3]);
   }
 
-  // Lane l32 of key block kb owns key kp + 32 kb + l32.
+  // Lane l32 of key block kb owns key kp + 32 kb + l32.  The final rows go
+  // out through LDS (tile sQ[w] or sO[w - 4], free once every wave is past
+  // its last step).
+  __syncthreads();
   const int which = w < 4 ? 1 : 0;  // 0: dK, 1: dV
   const float sc = w < 4 ? (DROP ? a.drop.inv : 1.f) : a.scale;
+  char* const stage = w < 4 ? sQ[w] : sO[w - 4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kp + 32 * kb + l32;
     if (a.nsplit == 1) {
       bf16* dst = reinterpret_cast<bf16*>(which ? a.dv : a.dk) + (size_t)bkv * slab;
-      store_rows<bf16, D>(dst, key, N, acc[kb], sc);
+      store_rows_lds<D>(dst, kp + 32 * kb, N, acc[kb], sc, stage);
     } else {
       const size_t ps = (size_t)a.B * a.Hkv * slab;  // elements of one partial tensor
       store_rows<float, D>(a.part + (2 * sp + which) * ps + (size_t)bkv * slab, key, N, acc[kb], sc);
@@ -985,7 +989,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     step(j + 1, sK1, sV1, sK0, sV0, Any());
   }
 
-  store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);
+  if constexpr (sizeof(T) == 2) {
+    // The tiles are free after the last step's barrier: wave w stages its rows
+    // in 32 rows of tile w / 2.
+    const int t2 = __builtin_amdgcn_readfirstlane(w) >> 1;
+    char* const stage = t2 == 0 ? sK0 : t2 == 1 ? sK1 : t2 == 2 ? sV0 : sV1;
+    store_rows_lds<D>(reinterpret_cast<bf16*>(a.dq) + (size_t)bh * slab, q0w, N, acc, a.scale,
+                      stage + (w & 1) * 32 * L::RB);
+  } else {
+    store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);
+  }
 }
 
 template <int D, bool CAUSAL, bool DROP>

@@ -360,6 +360,35 @@ __device__ __forceinline__ void store_rows(T* base, int row, int n, const f32x16
              s * acc[db][4 * g + 3]);
 }
 
+// The same for bf16 rows, through `lds`, a private region of the wave of 32
+// rows x 2 D bytes: each lane first writes its row's values there, then every
+// lane reads one 16-byte granule of a row, so that 2 D / 16 consecutive lanes
+// store one whole row (full cache lines instead of 8-byte pieces of 32 rows).
+// The 16-byte granules of row r are XOR-permuted by r so that the 32 rows of
+// a column group fall on different banks.  Called after the wave's last read
+// of the tiles that `lds` overlaps.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(bf16* base, int row0, int n, const f32x16* acc, float s, char* lds) {
+  constexpr int RB = 2 * D, G = RB / 16;  // bytes and 16-byte granules per row
+  const int lane = lane_id(), hf = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = db * 32 + 8 * g + 4 * hf;  // first of the four elements
+      char* p = lds + l32 * RB + (((col >> 3) ^ (l32 & (G - 1))) << 4) + (col & 7) * 2;
+      *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)(s * acc[db][4 * g]), (bf16)(s * acc[db][4 * g + 1]),
+                                             (bf16)(s * acc[db][4 * g + 2]), (bf16)(s * acc[db][4 * g + 3])};
+    }
+  constexpr int RPI = 64 / G;  // rows per store instruction
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / G, gr = lane % G;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RB + ((gr ^ (r & (G - 1))) << 4));
+    if (row0 + r < n) *reinterpret_cast<u32x4*>(base + (size_t)(row0 + r) * D + gr * 8) = v;
+  }
+}
+
 // ---------------------------------------------------------------- work order
 // Maps a linear workgroup index onto (unit, slice) with `units` units per
 // slice-step such that all workgroups of one unit land on the same XCD:
