@@ -796,7 +796,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a) {
     const int key = kp + 32 * kb + l32;
     if (a.nsplit == 1) {
       bf16* dst = reinterpret_cast<bf16*>(which ? a.dv : a.dk) + (size_t)bkv * slab;
-      store_rows_lds<D>(dst, kp + 32 * kb, N, acc[kb], sc, stage);
+      store_rows_lds<D, true>(dst, kp + 32 * kb, N, acc[kb], sc, stage);
     } else {
       const size_t ps = (size_t)a.B * a.Hkv * slab;  // elements of one partial tensor
       store_rows<float, D>(a.part + (2 * sp + which) * ps + (size_t)bkv * slab, key, N, acc[kb], sc);
@@ -994,7 +994,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int nqt) {
     // in 32 rows of tile w / 2.
     const int t2 = __builtin_amdgcn_readfirstlane(w) >> 1;
     char* const stage = t2 == 0 ? sK0 : t2 == 1 ? sK1 : t2 == 2 ? sV0 : sV1;
-    store_rows_lds<D>(reinterpret_cast<bf16*>(a.dq) + (size_t)bh * slab, q0w, N, acc, a.scale,
+    store_rows_lds<D, true>(reinterpret_cast<bf16*>(a.dq) + (size_t)bh * slab, q0w, N, acc, a.scale,
                       stage + (w & 1) * 32 * L::RB);
   } else {
     store_rows<T, D>(reinterpret_cast<T*>(a.dq) + (size_t)bh * slab, myq, N, acc, a.scale);

@@ -366,8 +366,10 @@ __device__ __forceinline__ void store_rows(T* base, int row, int n, const f32x16
 // store one whole row (full cache lines instead of 8-byte pieces of 32 rows).
 // The 16-byte granules of row r are XOR-permuted by r so that the 32 rows of
 // a column group fall on different banks.  Called after the wave's last read
-// of the tiles that `lds` overlaps.
-template <int D>
+// of the tiles that `lds` overlaps.  NT: with the non-temporal hint (rows
+// written once; measured on MI355X, the hint also suits O, which the backward
+// reads again).
+template <int D, bool NT = false>
 __device__ __forceinline__ void store_rows_lds(bf16* base, int row0, int n, const f32x16* acc, float s, char* lds) {
   constexpr int RB = 2 * D, G = RB / 16;  // bytes and 16-byte granules per row
   const int lane = lane_id(), hf = lane >> 5, l32 = lane & 31;
@@ -385,7 +387,11 @@ __device__ __forceinline__ void store_rows_lds(bf16* base, int row0, int n, cons
   for (int it = 0; it < 32 / RPI; ++it) {
     const int r = it * RPI + lane / G, gr = lane % G;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RB + ((gr ^ (r & (G - 1))) << 4));
-    if (row0 + r < n) *reinterpret_cast<u32x4*>(base + (size_t)(row0 + r) * D + gr * 8) = v;
+    u32x4* dst = reinterpret_cast<u32x4*>(base + (size_t)(row0 + r) * D + gr * 8);
+    if (row0 + r < n) {
+      if constexpr (NT) __builtin_nontemporal_store(v, dst);
+      else *dst = v;
+    }
   }
 }
 

@@ -323,7 +323,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     // in 32 rows of tile w / 2.
     const int t2 = __builtin_amdgcn_readfirstlane(w) >> 1;
     char* const stage = t2 == 0 ? sK0 : t2 == 1 ? sK1 : t2 == 2 ? sV0 : sV1;
-    store_rows_lds<D>(reinterpret_cast<bf16*>(a.o) + (size_t)bh * slab, q0w, N, acc, os,
+    store_rows_lds<D, true>(reinterpret_cast<bf16*>(a.o) + (size_t)bh * slab, q0w, N, acc, os,
                       stage + (w & 1) * 32 * L::RB);
   } else {
     store_rows<T, D>(reinterpret_cast<T*>(a.o) + (size_t)bh * slab, myq, N, acc, os);
