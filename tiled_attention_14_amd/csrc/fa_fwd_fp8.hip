@@ -63,6 +63,8 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   constexpr int TBK = kBc8 * KL::RB;        // 8 KB K or V tile
   constexpr int DB = kD8 / 32;
   __shared__ __attribute__((aligned(1024))) char sK0[TBK], sK1[TBK], sV0[TBK], sV1[TBK];
+  // Staging of the output rows of waves 4..7 (waves 0..3 use the tiles).
+  __shared__ __attribute__((aligned(1024))) char sX[4 * TBK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -222,7 +224,10 @@ __global__ __launch_bounds__(64 * kW8, 2) void fa_fwd_fp8_kernel(Fp8Args a) {
   }
 
   lsum += other_half(lsum);
-  store_rows<bf16, kD8>(reinterpret_cast<bf16*>(a.o) + (size_t)bh * N * kD8, myq, N, acc, a.vscale / lsum);
+  // The tiles are free after the last step's barrier; each wave stages its 32
+  // output rows (8 KB) in one of them or in sX.
+  char* const stage = w == 0 ? sK0 : w == 1 ? sK1 : w == 2 ? sV0 : w == 3 ? sV1 : sX + (w - 4) * TBK;
+  store_rows_lds<kD8, true>(reinterpret_cast<bf16*>(a.o) + (size_t)bh * N * kD8, q0w, N, acc, a.vscale / lsum, stage);
   if (hf == 0 && myq < N) a.lse[(size_t)bh * N + myq] = (m - kPExp + __log2f(lsum)) * kLn2;
 }
 
